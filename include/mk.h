@@ -1,0 +1,172 @@
+/*
+ * mk.h -- C ABI of libmk.so: one decode step through a stack of MoE
+ * transformer layers, run on an MI355X (gfx950) as ONE persistent kernel.
+ *
+ * What a step computes.  For each of L layers, for each of M rows (tokens):
+ *     (attention stacks)  h1 = h + Wo . GQA-Attn(RoPE(Wq x), RoPE(Wk x), Wv x),
+ *                         x = RMSNorm(h; attn_norm)
+ *     h2 = h1 + sum_{e in top-k} w_e . Wd_e (silu(Wg_e y) * Wu_e y)
+ *             + sum_shared Wd_s (silu(Wg_s y) * Wu_s y),   y = RMSNorm(h1; moe_norm)
+ * with router logits z = Wr y (+ bias), p = softmax(z), the top-k experts by
+ * p (equal values: lower expert id first) and w_e = p_e / sum_{top-k} p.
+ * The pages describe exactly this shape of work: a deep stack of MoE layers in
+ * which a router picks a few experts per token independently per layer, each
+ * layer's attention preceding its MoE, and the entire decode step run inside
+ * one program so that weight loads are no longer tied to per-operator kernel
+ * boundaries [P3 "TPU Megakernel Achieves 709 tokens/s on Kimi K3, Outpacing
+ * GB200", sections "The Key Innovation: 92 MoE Layers in a Single Pallas
+ * Kernel" and "Cross-Layer Weight Prefetching"; P2 myzaker article, section
+ * "把几百个小 kernel，焊成一个大程序"; P4 tanhow.com translation of the authors'
+ * post, paragraphs on kernel-boundary bubbles and on the megakernel].
+ * Definitions of the operators (RMSNorm with eps inside the root and a
+ * multiplicative gain, SwiGLU, half-split RoPE with inv_freq_i =
+ * theta^(-2i/hd), GQA head h reading kv head h / (H/G), scale 1/sqrt(hd)) are
+ * the standard ones; the pages give none.
+ *
+ * Storage.  Every matrix is row-major [out][in] (a linear layer's weight):
+ *   attn_norm, moe_norm  [d]                 dtype (fp32 or bf16)
+ *   wq [H*hd][d], wk [G*hd][d], wv [G*hd][d], wo [d][H*hd]   dtype
+ *   w_router [E][d] dtype;  b_router [E] fp32 or NULL
+ *   w_gate, w_up [E][F][d];  w_down [E][d][F]        dtype, experts packed
+ *   s_gate, s_up [n_shared][F][d];  s_down [n_shared][d][F]
+ * bf16 means the upper 16 bits of an IEEE binary32 (round-to-nearest-even
+ * from fp32 wherever the library rounds).  Hidden rows are fp32 [M][d].
+ * KV cache (bf16): k and v each [L][n_seq][G][capacity][hd], contiguous.
+ * Row r belongs to sequence r / rows_per_seq and sits at positions[r]; a
+ * step writes the row's k, v (RoPE applied to k, rounded to bf16) at that
+ * position and attends to cache positions 0..positions[r] of its sequence.
+ * Several rows of one sequence (a speculative-verify pass) must hold distinct
+ * positions; each row then sees the new rows of its sequence at lower or
+ * equal positions (causal).
+ *
+ * Ownership.  Weights, KV cache, hidden buffers and positions are device
+ * memory owned by the caller; the library never copies, repacks or frees
+ * them and only reads the weights.  The handle owns its workspace (scratch
+ * activations, barrier counters, the device copy of the weight-pointer
+ * table), allocated in mk_create and freed in mk_destroy.
+ *
+ * Errors.  Every call returns MK_OK (0) or a negative mk_status.  Argument
+ * checks that need no device data happen at once.  Conditions only the
+ * device can see (a position outside [0, capacity), two rows of one
+ * sequence at the same position, a grid barrier that does not complete) set
+ * a device error flag; the step then skips the affected writes and ends, and
+ * the next mk_sync returns the error and clears it.  mk_strerror describes a
+ * status; mk_last_error describes the most recent failure of this thread.
+ *
+ * Concurrency.  A handle's workspace is shared by its launches: do not run
+ * steps of one handle on two streams at once.  Several handles may share the
+ * same weights (e.g. batch 1 and batch 8 over one stack).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+
+typedef enum mk_status {
+  MK_OK = 0,
+  MK_ERR_INVALID_ARG = -1, /* NULL/aliased pointer, inconsistent sizes, bad position (device) */
+  MK_ERR_UNSUPPORTED = -2, /* shape or dtype outside what the kernels implement */
+  MK_ERR_DEVICE = -3,      /* no suitable gfx950 device, or one workgroup per CU cannot be co-resident */
+  MK_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
+  MK_ERR_TIMEOUT = -5      /* a grid barrier did not complete (device watchdog) */
+} mk_status;
+
+typedef enum mk_dtype { MK_F32 = 0, MK_BF16 = 1 } mk_dtype;
+
+typedef struct mk_config {
+  int32_t n_layers;        /* L >= 1 */
+  int32_t d_model;         /* d: row length 1, 2, 4 or 8 KiB in the weight dtype */
+  int32_t n_experts;       /* E, 1..64 */
+  int32_t top_k;           /* k, 1..min(E, 8) */
+  int32_t n_shared;        /* always-on shared experts, weight 1; 0..4 */
+  int32_t d_ff;            /* F: row length of w_down, 1, 2, 4 or 8 KiB */
+  int32_t dtype;           /* mk_dtype of matrices and norm gains */
+  int32_t has_router_bias; /* b_router must be non-NULL when set */
+  float rms_eps;           /* > 0 */
+  int32_t has_attn;        /* 0: MoE-only layers (h1 = h) */
+  int32_t n_heads;         /* H (attention stacks) */
+  int32_t n_kv_heads;      /* G, H % G == 0, H / G <= 8 */
+  int32_t head_dim;        /* hd = 128 */
+  float rope_theta;        /* > 0 */
+  int32_t rows;            /* M, 1..64, fixed per handle */
+  int32_t rows_per_seq;    /* 1 for decode; > 1 for a verify pass; divides M */
+  int32_t kv_capacity;     /* positions per sequence in the cache (attention stacks) */
+} mk_config;
+
+typedef struct mk_layer_weights {
+  const void* attn_norm;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* moe_norm;
+  const void* w_router;
+  const float* b_router;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
+} mk_layer_weights;
+
+typedef struct mk_kv_cache {
+  void* k;          /* [L][n_seq][G][capacity][hd] bf16, device */
+  void* v;
+  int32_t n_seq;    /* >= rows / rows_per_seq */
+  int32_t capacity; /* == cfg.kv_capacity */
+} mk_kv_cache;
+
+typedef struct mk_info {
+  int32_t n_cu;              /* workgroups in the persistent grid (one per CU) */
+  int32_t threads;           /* threads per workgroup */
+  int32_t lds_bytes;         /* dynamic LDS per workgroup */
+  int32_t barriers_per_step; /* grid barriers one step executes */
+  int32_t attn_splits;       /* KV splits per (sequence, kv head) */
+  int64_t workspace_bytes;   /* device memory owned by the handle */
+} mk_info;
+
+typedef struct mk_handle mk_handle;
+
+/* Validate cfg, bind the weights of all L layers (host array `layers` of
+ * device pointers, read at this call only), allocate the workspace.  On
+ * success *out receives the handle.  Errors: INVALID_ARG, UNSUPPORTED,
+ * DEVICE, HIP. */
+int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** out);
+
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL = default
+ * stream) and return at once.  hidden_in [M][d] fp32, positions [M] int32,
+ * hidden_out [M][d] fp32 are device pointers; hidden_out must not overlap
+ * hidden_in.  kv may be NULL only for stacks without attention.  Errors:
+ * INVALID_ARG, HIP. */
+int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+                   float* hidden_out, void* stream);
+
+/* Free the workspace and the handle.  NULL is accepted. */
+int mk_destroy(mk_handle* h);
+
+/* Wait for `stream` and report (then clear) any device-side error of this
+ * handle's steps: TIMEOUT or INVALID_ARG. */
+int mk_sync(mk_handle* h, void* stream);
+
+/* Record routing per step into device buffers (any may be NULL; all NULL
+ * turns tracing off): ids [L][M][k] int32, w [L][M][k] fp32 (renormalised
+ * weights, in top-k order), logits [L][M][E] fp32 (after bias). */
+int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits);
+
+/* Launch geometry and workspace size of a handle. */
+int mk_get_info(const mk_handle* h, mk_info* info);
+
+const char* mk_strerror(int status);
+const char* mk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
