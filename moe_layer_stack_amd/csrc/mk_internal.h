@@ -1,0 +1,102 @@
+// mk_internal.h -- structures shared by the host runtime and the persistent
+// decode kernel.  Not part of the public ABI (include/mk.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace mk {
+
+constexpr int kThreads = 256;           // 4 waves of 64 lanes: one wave per SIMD
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileBytes = 8192;        // weight tile streamed through the LDS ring
+constexpr int kChunk = 1024;            // one global_load_lds: 64 lanes x 16 B
+constexpr int kMaxRows = 64;            // M
+constexpr int kMaxExperts = 64;         // E (one lane per expert in top-k)
+constexpr int kMaxTopK = 8;
+constexpr int kMaxShared = 4;
+constexpr int kMaxQ = 32;               // query vectors per attention task
+constexpr int kAttnTile = 32;           // positions per KV tile (hd = 128 bf16 -> 8 KB)
+constexpr int kLdsTotal = 160 * 1024;
+constexpr int kPartBytes = 8 * 1024;
+constexpr int kMiscBytes = 8 * 1024;
+
+// device error flag bits
+enum : unsigned { kErrTimeout = 1u, kErrPosition = 2u, kErrDupPosition = 4u };
+
+// Device copy of one layer's weight pointers.
+struct DevLayer {
+  const void* attn_norm;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* moe_norm;
+  const void* w_router;
+  const float* b_router;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
+};
+
+// Byte offsets of one layer's activation scratch (all fp32, 256-byte aligned,
+// every location written at most once per launch).
+struct ActLayout {
+  size_t h1;      // [M][d]
+  size_t qkv;     // [M][(H+2G)*hd]   raw projections (RoPE applied by the reader)
+  size_t part;    // [n_seq][G][S][Q][hd+2]  attention partials (m, l, acc)
+  size_t o;       // [M][H*hd]
+  size_t logits;  // [M][E]
+  size_t a_s;     // [M][n_shared][F]  shared SwiGLU activations
+  size_t a;       // [M][k][F]         routed SwiGLU activations (slot = top-k rank)
+  size_t h2;      // [M][d]            layer output (next layer's input)
+  size_t stride;  // bytes per layer
+};
+
+// Barrier / counter block (each word on its own 256-byte line).
+struct SyncLayout {
+  static constexpr int kLine = 64;  // in uint32 words
+  static constexpr int kGlobal = 0;
+  static constexpr int kEpoch = 1 * kLine;
+  static constexpr int kErr = 2 * kLine;
+  static constexpr int kGroup = 4 * kLine;   // 8 group counters
+  static constexpr int kFlag = 12 * kLine;   // 8 group release flags
+  static constexpr int kWords = 20 * kLine;
+};
+
+struct KParams {
+  // shapes
+  int L, d, E, k, S, F;
+  int H, G, hd, M, rps, n_seq, cap;
+  int attn, has_bias, wide;  // wide: weights are fp32
+  float eps, theta;
+  int n_splits;              // KV splits per (seq, kv head)
+  int q_per_task;            // rps * (H / G)
+  // launch geometry / LDS carve-up
+  int n_cu;
+  int ring_tiles;
+  int x_bytes;               // LDS x region
+  int barriers;              // grid barriers per step
+  long long timeout_ticks;   // s_memrealtime ticks (100 MHz) before a barrier gives up
+  // pointers
+  const DevLayer* layers;
+  const float* hidden_in;
+  float* hidden_out;
+  const int* positions;
+  uint16_t* kcache;
+  uint16_t* vcache;
+  char* act;
+  ActLayout al;
+  unsigned* sync;            // SyncLayout
+  unsigned* attn_cnt;        // [L][n_seq][G]
+  int* t_ids;
+  float* t_w;
+  float* t_logits;
+};
+
+}  // namespace mk
+
+extern "C" int mk_launch_kernel(const mk::KParams* p, void* stream);

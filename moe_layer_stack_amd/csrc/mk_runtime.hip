@@ -1,0 +1,338 @@
+// mk_runtime.hip -- host side of libmk.so: argument validation, workspace,
+// the device copy of the weight-pointer table, the cooperative launch, and
+// device-error reporting.  See include/mk.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "mk.h"
+#include "mk_internal.h"
+
+using mk::ActLayout;
+using mk::DevLayer;
+using mk::KParams;
+using mk::SyncLayout;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool is_row_size_ok(long long bytes) {
+  return bytes == 1024 || bytes == 2048 || bytes == 4096 || bytes == 8192;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct mk_handle {
+  mk_config cfg;
+  int device;
+  int n_cu;
+  int n_splits;
+  int barriers;
+  int ring_tiles;
+  int x_bytes;
+  ActLayout al;
+  DevLayer* d_layers = nullptr;
+  char* d_act = nullptr;
+  unsigned* d_sync = nullptr;
+  unsigned* d_attn_cnt = nullptr;
+  size_t act_bytes = 0;
+  size_t attn_cnt_bytes = 0;
+  int32_t* t_ids = nullptr;
+  float* t_w = nullptr;
+  float* t_logits = nullptr;
+};
+
+namespace {
+
+int validate(const mk_config* c) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->n_layers < 1) return fail(MK_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (c->dtype != MK_F32 && c->dtype != MK_BF16) return fail(MK_ERR_UNSUPPORTED, "dtype must be MK_F32 or MK_BF16");
+  const int es = c->dtype == MK_F32 ? 4 : 2;
+  if (c->d_model < 1 || !is_row_size_ok((long long)c->d_model * es))
+    return fail(MK_ERR_UNSUPPORTED, "d_model rows must be 1, 2, 4 or 8 KiB (d=%d)", c->d_model);
+  if (c->d_ff < 1 || !is_row_size_ok((long long)c->d_ff * es))
+    return fail(MK_ERR_UNSUPPORTED, "d_ff rows must be 1, 2, 4 or 8 KiB (F=%d)", c->d_ff);
+  const int rpt_d = 8192 / (c->d_model * es);
+  if (c->d_ff % rpt_d) return fail(MK_ERR_UNSUPPORTED, "d_ff must be a multiple of %d", rpt_d);
+  const int rpt_f = 8192 / (c->d_ff * es);
+  if (c->d_model % rpt_f) return fail(MK_ERR_UNSUPPORTED, "d_model must be a multiple of %d", rpt_f);
+  if (c->n_experts < 1 || c->n_experts > mk::kMaxExperts) return fail(MK_ERR_UNSUPPORTED, "n_experts must be 1..64");
+  if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > mk::kMaxTopK)
+    return fail(MK_ERR_UNSUPPORTED, "top_k must be 1..min(n_experts, 8)");
+  if (c->n_shared < 0 || c->n_shared > mk::kMaxShared) return fail(MK_ERR_UNSUPPORTED, "n_shared must be 0..4");
+  if (!(c->rms_eps > 0.f)) return fail(MK_ERR_INVALID_ARG, "rms_eps must be > 0");
+  if (c->rows < 1 || c->rows > 8) return fail(MK_ERR_UNSUPPORTED, "rows must be 1..8 in this build");
+  if (c->rows_per_seq < 1 || c->rows % c->rows_per_seq) return fail(MK_ERR_INVALID_ARG, "rows_per_seq must divide rows");
+  if (c->has_attn) {
+    if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
+      return fail(MK_ERR_INVALID_ARG, "n_heads must be a positive multiple of n_kv_heads");
+    if (c->head_dim != 128) return fail(MK_ERR_UNSUPPORTED, "head_dim must be 128");
+    if (c->rows_per_seq * (c->n_heads / c->n_kv_heads) > mk::kMaxQ)
+      return fail(MK_ERR_UNSUPPORTED, "rows_per_seq * n_heads / n_kv_heads must be <= %d", mk::kMaxQ);
+    if (!is_row_size_ok((long long)c->n_heads * c->head_dim * es))
+      return fail(MK_ERR_UNSUPPORTED, "n_heads*head_dim rows must be 1, 2, 4 or 8 KiB");
+    if (c->d_model % (8192 / (c->n_heads * c->head_dim * es)))
+      return fail(MK_ERR_UNSUPPORTED, "d_model must be a multiple of the rows per Wo tile");
+    if (!(c->rope_theta > 0.f)) return fail(MK_ERR_INVALID_ARG, "rope_theta must be > 0");
+    if (c->kv_capacity < 1) return fail(MK_ERR_INVALID_ARG, "kv_capacity must be >= 1");
+    if ((long long)c->kv_capacity * c->head_dim * 2 >= (1LL << 31))
+      return fail(MK_ERR_UNSUPPORTED, "kv_capacity too large");
+  }
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_strerror(int status) {
+  switch (status) {
+    case MK_OK: return "success";
+    case MK_ERR_INVALID_ARG: return "invalid argument";
+    case MK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MK_ERR_DEVICE: return "no suitable gfx950 device or co-residency not possible";
+    case MK_ERR_HIP: return "HIP runtime error";
+    case MK_ERR_TIMEOUT: return "grid barrier timed out on the device";
+    default: return "unknown status";
+  }
+}
+
+const char* mk_last_error(void) { return g_last_error.c_str(); }
+
+int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** out) {
+  if (!out) return fail(MK_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!layers) return fail(MK_ERR_INVALID_ARG, "layers is NULL");
+  const mk_config& c = *cfg;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const mk_layer_weights& w = layers[l];
+    if (!w.moe_norm || !w.w_router || !w.w_gate || !w.w_up || !w.w_down)
+      return fail(MK_ERR_INVALID_ARG, "layer %d: MoE weight pointer is NULL", l);
+    if (c.has_router_bias && !w.b_router) return fail(MK_ERR_INVALID_ARG, "layer %d: b_router is NULL", l);
+    if (c.n_shared > 0 && (!w.s_gate || !w.s_up || !w.s_down))
+      return fail(MK_ERR_INVALID_ARG, "layer %d: shared expert pointer is NULL", l);
+    if (c.has_attn && (!w.attn_norm || !w.wq || !w.wk || !w.wv || !w.wo))
+      return fail(MK_ERR_INVALID_ARG, "layer %d: attention weight pointer is NULL", l);
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MK_ERR_DEVICE, "no HIP device");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MK_ERR_DEVICE, "hipGetDeviceProperties failed");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MK_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  if (!prop.cooperativeLaunch) return fail(MK_ERR_DEVICE, "device lacks cooperative launch");
+  if (prop.maxSharedMemoryPerMultiProcessor < (size_t)mk::kLdsTotal)
+    return fail(MK_ERR_DEVICE, "device has %zu bytes of LDS per CU, need %d", prop.maxSharedMemoryPerMultiProcessor,
+                mk::kLdsTotal);
+
+  mk_handle* h = new (std::nothrow) mk_handle();
+  if (!h) return fail(MK_ERR_HIP, "out of host memory");
+  h->cfg = c;
+  h->device = dev;
+  h->n_cu = prop.multiProcessorCount;
+  const int M = c.rows;
+  const int n_seq = M / c.rows_per_seq;
+  const int H = c.has_attn ? c.n_heads : 0, G = c.has_attn ? c.n_kv_heads : 0, hd = c.has_attn ? c.head_dim : 0;
+  h->n_splits = 1;
+  if (c.has_attn) {
+    int s = h->n_cu / (n_seq * G);
+    if (s < 1) s = 1;
+    int maxs = (c.kv_capacity + mk::kAttnTile - 1) / mk::kAttnTile;
+    if (s > maxs) s = maxs;
+    h->n_splits = s;
+  }
+  h->barriers = c.n_layers * (c.has_attn ? 6 : 3) - 1;
+  // LDS: x region sized for the largest fp32 activation block (capped), ring gets the rest
+  long long xneed = (long long)M * c.d_model;
+  if (c.has_attn && (long long)M * H * hd > xneed) xneed = (long long)M * H * hd;
+  if ((long long)M * (c.n_shared + c.top_k) * c.d_ff > xneed) xneed = (long long)M * (c.n_shared + c.top_k) * c.d_ff;
+  xneed *= 4;
+  const long long xattn = (long long)(mk::kMaxQ * 128 + mk::kMaxQ * 32) * 4;
+  if (xneed < xattn) xneed = xattn;
+  if (xneed > 64 * 1024) xneed = 64 * 1024;
+  h->x_bytes = (int)((xneed + 1023) / 1024 * 1024);
+  int ring = (mk::kLdsTotal - h->x_bytes - mk::kPartBytes - mk::kMiscBytes) / mk::kTileBytes;
+  if (ring > 24) ring = 24;
+  h->ring_tiles = ring;
+  // activation scratch per layer
+  const int E = c.n_experts, k = c.top_k, S = c.n_shared, F = c.d_ff, d = c.d_model;
+  const int Q = c.has_attn ? c.rows_per_seq * (H / G) : 0;
+  size_t off = 0;
+  ActLayout al{};
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  al.h1 = take((size_t)M * d * 4);
+  al.qkv = take((size_t)M * (H + 2 * G) * hd * 4);
+  al.part = take((size_t)n_seq * G * h->n_splits * Q * (hd + 2) * 4);
+  al.o = take((size_t)M * H * hd * 4);
+  al.logits = take((size_t)M * E * 4);
+  al.a_s = take((size_t)M * S * F * 4);
+  al.a = off;  // must directly follow a_s (phase DOWN reads both as one block)
+  off = al.a + (size_t)M * k * F * 4;
+  if (S > 0 && al.a != al.a_s + (size_t)M * S * F * 4) {
+    // a_s size is a multiple of 256 when F*4 is, which validate() guarantees
+    delete h;
+    return fail(MK_ERR_UNSUPPORTED, "internal layout error");
+  }
+  off = align256(off);
+  al.h2 = take((size_t)M * d * 4);
+  al.stride = align256(off);
+  h->al = al;
+  h->act_bytes = al.stride * c.n_layers;
+  h->attn_cnt_bytes = c.has_attn ? (size_t)c.n_layers * n_seq * G * 4 : 256;
+
+  auto cleanup = [&]() {
+    if (h->d_layers) (void)hipFree(h->d_layers);
+    if (h->d_act) (void)hipFree(h->d_act);
+    if (h->d_sync) (void)hipFree(h->d_sync);
+    if (h->d_attn_cnt) (void)hipFree(h->d_attn_cnt);
+    delete h;
+  };
+  std::vector<DevLayer> hl(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const mk_layer_weights& w = layers[l];
+    hl[l] = DevLayer{w.attn_norm, w.wq, w.wk, w.wv, w.wo, w.moe_norm, w.w_router, w.b_router,
+                     w.w_gate, w.w_up, w.w_down, w.s_gate, w.s_up, w.s_down};
+  }
+  if (hipMalloc(&h->d_layers, sizeof(DevLayer) * c.n_layers) != hipSuccess ||
+      hipMalloc(&h->d_act, h->act_bytes) != hipSuccess ||
+      hipMalloc(&h->d_sync, SyncLayout::kWords * 4) != hipSuccess ||
+      hipMalloc(&h->d_attn_cnt, h->attn_cnt_bytes) != hipSuccess) {
+    cleanup();
+    return fail(MK_ERR_HIP, "workspace allocation failed");
+  }
+  if (hipMemcpy(h->d_layers, hl.data(), sizeof(DevLayer) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess ||
+      hipMemset(h->d_attn_cnt, 0, h->attn_cnt_bytes) != hipSuccess ||
+      hipMemset(h->d_act, 0, h->act_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    cleanup();
+    return fail(MK_ERR_HIP, "workspace initialisation failed");
+  }
+  *out = h;
+  return MK_OK;
+}
+
+int mk_destroy(mk_handle* h) {
+  if (!h) return MK_OK;
+  int rc = MK_OK;
+  if (h->d_layers && hipFree(h->d_layers) != hipSuccess) rc = MK_ERR_HIP;
+  if (h->d_act && hipFree(h->d_act) != hipSuccess) rc = MK_ERR_HIP;
+  if (h->d_sync && hipFree(h->d_sync) != hipSuccess) rc = MK_ERR_HIP;
+  if (h->d_attn_cnt && hipFree(h->d_attn_cnt) != hipSuccess) rc = MK_ERR_HIP;
+  delete h;
+  return rc == MK_OK ? MK_OK : fail(rc, "hipFree failed");
+}
+
+int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits) {
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  h->t_ids = ids;
+  h->t_w = w;
+  h->t_logits = logits;
+  return MK_OK;
+}
+
+int mk_get_info(const mk_handle* h, mk_info* info) {
+  if (!h || !info) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  info->n_cu = h->n_cu;
+  info->threads = mk::kThreads;
+  info->lds_bytes = h->ring_tiles * mk::kTileBytes + h->x_bytes + mk::kPartBytes + mk::kMiscBytes;
+  info->barriers_per_step = h->barriers;
+  info->attn_splits = h->n_splits;
+  info->workspace_bytes =
+      (int64_t)(h->act_bytes + SyncLayout::kWords * 4 + h->attn_cnt_bytes + sizeof(DevLayer) * h->cfg.n_layers);
+  return MK_OK;
+}
+
+int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+                   float* hidden_out, void* stream) {
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  if (!hidden_in || !hidden_out || !positions) return fail(MK_ERR_INVALID_ARG, "NULL device pointer");
+  const mk_config& c = h->cfg;
+  const size_t hb = (size_t)c.rows * c.d_model * 4;
+  const char* a0 = reinterpret_cast<const char*>(hidden_in);
+  const char* b0 = reinterpret_cast<const char*>(hidden_out);
+  if (a0 < b0 + hb && b0 < a0 + hb) return fail(MK_ERR_INVALID_ARG, "hidden_out overlaps hidden_in");
+  const int n_seq = c.rows / c.rows_per_seq;
+  if (c.has_attn) {
+    if (!kv || !kv->k || !kv->v) return fail(MK_ERR_INVALID_ARG, "kv cache required for attention stacks");
+    if (kv->n_seq < n_seq) return fail(MK_ERR_INVALID_ARG, "kv->n_seq (%d) < sequences per step (%d)", kv->n_seq, n_seq);
+    if (kv->capacity != c.kv_capacity)
+      return fail(MK_ERR_INVALID_ARG, "kv->capacity (%d) != cfg.kv_capacity (%d)", kv->capacity, c.kv_capacity);
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return fail(MK_ERR_INVALID_ARG, "current device differs from the handle's device");
+  KParams p{};
+  p.L = c.n_layers; p.d = c.d_model; p.E = c.n_experts; p.k = c.top_k; p.S = c.n_shared; p.F = c.d_ff;
+  p.attn = c.has_attn ? 1 : 0;
+  p.H = c.has_attn ? c.n_heads : 0; p.G = c.has_attn ? c.n_kv_heads : 1; p.hd = c.has_attn ? c.head_dim : 0;
+  p.M = c.rows; p.rps = c.rows_per_seq; p.n_seq = n_seq;
+  p.cap = c.has_attn ? kv->capacity : 0;
+  p.has_bias = c.has_router_bias ? 1 : 0;
+  p.wide = c.dtype == MK_F32 ? 1 : 0;
+  p.eps = c.rms_eps; p.theta = c.rope_theta;
+  p.n_splits = h->n_splits;
+  p.q_per_task = c.has_attn ? c.rows_per_seq * (c.n_heads / c.n_kv_heads) : 0;
+  p.n_cu = h->n_cu;
+  p.ring_tiles = h->ring_tiles;
+  p.x_bytes = h->x_bytes;
+  p.barriers = h->barriers;
+  p.timeout_ticks = 200LL * 1000 * 1000;  // 2 s of the 100 MHz realtime counter
+  p.layers = h->d_layers;
+  p.hidden_in = hidden_in;
+  p.hidden_out = hidden_out;
+  p.positions = positions;
+  p.kcache = c.has_attn ? static_cast<uint16_t*>(kv->k) : nullptr;
+  p.vcache = c.has_attn ? static_cast<uint16_t*>(kv->v) : nullptr;
+  p.act = h->d_act;
+  p.al = h->al;
+  p.sync = h->d_sync;
+  p.attn_cnt = h->d_attn_cnt;
+  p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
+  int e = mk_launch_kernel(&p, stream);
+  if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
+  if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  return MK_OK;
+}
+
+int mk_sync(mk_handle* h, void* stream) {
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MK_ERR_HIP, "stream synchronize failed: %s", hipGetErrorString(e));
+  unsigned err = 0;
+  e = hipMemcpy(&err, h->d_sync + SyncLayout::kErr, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MK_ERR_HIP, "reading the device error flag failed: %s", hipGetErrorString(e));
+  if (err == 0) return MK_OK;
+  // reset barrier state and counters so the handle can run again
+  if (hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess ||
+      hipMemset(h->d_attn_cnt, 0, h->attn_cnt_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return fail(MK_ERR_HIP, "resetting the barrier state failed");
+  if (err & mk::kErrTimeout) return fail(MK_ERR_TIMEOUT, "a grid barrier timed out (device flag 0x%x)", err);
+  return fail(MK_ERR_INVALID_ARG, "a position was outside the cache or repeated within a sequence (flag 0x%x)", err);
+}
+
+}  // extern "C"

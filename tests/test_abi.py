@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/mk.h declares, and rejects bad arguments before touching a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def mk():
+    import moe_layer_stack_amd as mk
+    from moe_layer_stack_amd import build
+    if not os.path.exists(os.path.join(ROOT, "moe_layer_stack_amd", "libmk.so")):
+        build.build()
+    mk.lib()
+    return mk
+
+
+def declared(header):
+    src = open(os.path.join(ROOT, "include", header)).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(mk_[a-z_]+|synth_[a-z0-9_]+)\s*\(", src))
+
+
+def test_every_declared_function_is_exported(mk):
+    names = declared("mk.h")
+    assert {"mk_create", "mk_decode_step", "mk_destroy"} <= names
+    L = C.CDLL(os.path.join(ROOT, "moe_layer_stack_amd", "libmk.so"))
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(mk.EXPORTS) == names
+
+
+def test_synth_exports(syn):
+    L = C.CDLL(syn.LIB)
+    for n in declared("synth.h"):
+        assert hasattr(L, n), n
+
+
+def test_struct_sizes_match_header(mk):
+    # mk_config: 17 x 4-byte fields; mk_layer_weights: 14 pointers; mk_kv_cache: 2 pointers + 2 ints
+    assert C.sizeof(mk.mk_config) == 17 * 4
+    assert C.sizeof(mk.mk_layer_weights) == 14 * 8
+    assert C.sizeof(mk.mk_kv_cache) == 24
+    assert C.sizeof(mk.mk_info) == 24 + 8
+
+
+def test_strerror(mk):
+    assert mk.mk_strerror(mk.MK_OK) == "success"
+    assert "timed out" in mk.mk_strerror(mk.MK_ERR_TIMEOUT)
+    assert mk.mk_strerror(-99) == "unknown status"
+
+
+def _cfg(mk, **kw):
+    c = dict(n_layers=2, d_model=256, n_experts=8, top_k=2, n_shared=0, d_ff=512, dtype=mk.MK_F32,
+             has_router_bias=0, rms_eps=1e-6, has_attn=0, n_heads=0, n_kv_heads=0, head_dim=0, rope_theta=1e6,
+             rows=1, rows_per_seq=1, kv_capacity=0)
+    c.update(kw)
+    return mk.mk_config(**c)
+
+
+def _layers(n):
+    from moe_layer_stack_amd import mk_layer_weights
+    fake = 0x1000
+    return [mk_layer_weights(None, None, None, None, None, fake, fake, None, fake, fake, fake, None, None, None)
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_layers=0), -1),
+    (dict(dtype=7), -2),
+    (dict(d_model=300), -2),           # row not 1/2/4/8 KiB
+    (dict(d_ff=100), -2),
+    (dict(n_experts=65), -2),
+    (dict(top_k=9, n_experts=16), -2),
+    (dict(top_k=3, n_experts=2), -2),
+    (dict(n_shared=5), -2),
+    (dict(rms_eps=0.0), -1),
+    (dict(rows=9), -2),
+    (dict(rows=4, rows_per_seq=3), -1),
+    (dict(has_attn=1, n_heads=3, n_kv_heads=2, head_dim=128, d_model=256, kv_capacity=16), -1),
+    (dict(has_attn=1, n_heads=2, n_kv_heads=1, head_dim=64, kv_capacity=16), -2),
+])
+def test_create_rejects_bad_config(mk, kw, status):
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_create(_cfg(mk, **kw), _layers(max(1, kw.get("n_layers", 2))))
+    assert ei.value.status == status, str(ei.value)
+
+
+def test_create_rejects_null_weights(mk):
+    from moe_layer_stack_amd import mk_layer_weights
+    lw = [mk_layer_weights() for _ in range(2)]
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_create(_cfg(mk), lw)
+    assert ei.value.status == mk.MK_ERR_INVALID_ARG and "NULL" in mk.mk_last_error()
+
+
+def test_create_requires_bias_when_configured(mk):
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_create(_cfg(mk, has_router_bias=1), _layers(2))
+    assert ei.value.status == mk.MK_ERR_INVALID_ARG and "b_router" in mk.mk_last_error()
+
+
+def test_decode_step_rejects_null_handle(mk):
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_decode_step(None, 0x1000, 0x2000, None, 0x3000)
+    assert ei.value.status == mk.MK_ERR_INVALID_ARG
+
+
+def test_destroy_accepts_null(mk):
+    assert mk.mk_destroy(None) == mk.MK_OK
+
+
+def test_create_without_gpu_reports_device(mk):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_create(_cfg(mk), _layers(2))
+    assert ei.value.status == mk.MK_ERR_DEVICE
