@@ -1,0 +1,236 @@
+"""Decode-step benchmark of the MI355X MoE megakernel (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (synthetic, seeded): the 92-layer stack, d=4096, 64 routed experts
+top-8 + 1 shared expert (F=1024, SwiGLU), GQA attention (32 q heads, 8 kv
+heads, head_dim 128, RoPE theta 1e6) over a bf16 KV cache of 4096 past
+positions; bf16 weights N(0, 0.02) (158 GB resident in HBM, far above the
+256 MB Infinity Cache), fp32 accumulation.  Each step feeds its output back
+as the next step's input and advances the positions.
+
+Prints ONE JSON line.  value = decode tokens/s at batch 1 (whole job, one
+GPU).  The batch-8 figures over the same weights are reported under
+"batch8".  roofline: algorithmic bytes of one step (attention weights, router
+weights, union of activated experts + shared expert, KV read) divided by the
+kernel's average duration from HIP events on its stream, against 8 TB/s.
+cpu_baseline: the CPU oracle timed on a bounded sample of layers of the same
+step, scaled to tokens/s.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "decode tokens/s at batch 1 and 8; achieved HBM GB/s as % of MI355X peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "moe_layer_stack_amd", "csrc"))):
+        with open(os.path.join(ROOT, "moe_layer_stack_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(w, M, n_seq, union_per_layer, kv_read_positions):
+    """Algorithmic bytes of one step: weights that must be streamed (attention,
+    router, union of routed experts + shared) plus KV rows read."""
+    es = 2 if w.dtype == 1 else 4
+    be = 3 * w.d * w.F * es
+    attn = (2 * w.d * w.H * w.hd + 2 * w.d * w.G * w.hd) * es if w.has_attn else 0
+    router = w.d * w.E * es
+    total = 0
+    for u in union_per_layer:
+        total += attn + router + (u + w.n_shared) * be
+    if w.has_attn:
+        total += len(union_per_layer) * kv_read_positions * 2 * w.G * w.hd * 2
+    return total
+
+
+def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union):
+    """Time `steps` decode steps of batch M (after `warmup`).  Returns dict."""
+    import numpy as np
+    cfg = st.config(rows=M, rows_per_seq=rows_per_seq)
+    h = mk.mk_create(cfg, st.layer_weights())
+    info = mk.mk_get_info(h)
+    stream = torch.cuda.current_stream()
+    n_seq = M // rows_per_seq
+    total = warmup + steps
+    p0 = w.past
+    pos = np.array([[p0 + t * rows_per_seq + (r % rows_per_seq) for r in range(M)] for t in range(total)],
+                   dtype=np.int32)
+    pos_d = torch.as_tensor(pos, device="cuda")
+    bufs = [st.hidden(0)[:M].contiguous(), torch.empty(M, w.d, dtype=torch.float32, device="cuda")]
+    kv = mk.mk_kv_cache(st.kc.data_ptr(), st.vc.data_ptr(), st.w.n_seq, st.w.capacity)
+    ids = torch.zeros(total, st.L, M, w.k, dtype=torch.int32, device="cuda") if trace_union else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    sp = stream.cuda_stream
+    for t in range(total):
+        if trace_union:
+            mk.mk_set_trace(h, ids[t].data_ptr(), 0, 0)
+        timed = t >= warmup
+        if t == warmup:
+            torch.cuda.synchronize()
+            t_wall0 = time.perf_counter()
+        if timed:
+            ev[t - warmup][0].record(stream)
+        mk.mk_decode_step(h, bufs[t % 2].data_ptr(), pos_d[t].data_ptr(), kv, bufs[(t + 1) % 2].data_ptr(), sp)
+        if timed:
+            ev[t - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    rc = mk.mk_sync(h, sp)
+    if rc != mk.MK_OK:
+        raise mk.MkError(rc, mk.mk_last_error())
+    durs = np.array([a.elapsed_time(b) for a, b in ev])  # ms, per launch
+    if trace_union:
+        idn = ids.cpu().numpy()
+        unions = [[len(np.unique(idn[t, l])) for l in range(st.L)] for t in range(total)]
+    else:
+        unions = [[w.k] * st.L for _ in range(total)]
+    byts = [step_bytes(w, M, n_seq, unions[t], 0) + st.L * n_seq * (int(pos[t].max()) + 1) * 2 * w.G * w.hd * 2
+            for t in range(warmup, total)]
+    mk.mk_destroy(h)
+    ms = float(durs.mean())
+    gbps = float(np.mean(byts)) / (ms * 1e-3) / 1e9
+    finite = bool(torch.isfinite(bufs[total % 2]).all().item())
+    return dict(M=M, ms_per_step=ms, ms_p10=float(np.percentile(durs, 10)), ms_p90=float(np.percentile(durs, 90)),
+                wall_ms_per_step=t_wall * 1e3 / steps, tok_s=M / (ms * 1e-3), bytes_per_step=float(np.mean(byts)),
+                achieved_gbps=gbps, frac=gbps / PEAK_HBM_GBPS,
+                union_mean=float(np.mean([np.mean(u) for u in unions[warmup:]])), barriers=info.barriers_per_step,
+                finite=finite)
+
+
+def cpu_baseline(torch, st, w, n_layers_sample):
+    """The CPU oracle (as it stands) on the first layers of a batch-1 step:
+    host copies of the touched tensors are made before the timer starts."""
+    import numpy as np
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_util import dims_of, oracle_layer
+    dims = dims_of(w)
+    h = st.hidden(0)[:1].cpu().numpy().astype(np.float64)
+    pos = [w.past]
+    t_compute = 0.0
+    for l in range(n_layers_sample):
+        H = st.host_layer(l, experts=[])  # attention, router, shared
+        kv = oracle.OracleKV(st.to_host(st.kc[l, :1]), st.to_host(st.vc[l, :1]))
+        ly = oracle_layer(H)
+        t0 = time.perf_counter()
+        h1 = oracle.attn_block(dims, ly, h, pos, kv)
+        _, ids, wts, _ = oracle.route(dims, ly, h1)
+        t_compute += time.perf_counter() - t0
+        H = st.host_layer(l, experts=ids[0])
+        ly = oracle_layer(H)
+        t0 = time.perf_counter()
+        h = oracle.moe_block(dims, ly, h1, ids, wts)
+        t_compute += time.perf_counter() - t0
+    per_layer = t_compute / n_layers_sample
+    step_s = per_layer * w.L
+    return dict(value=1.0 / step_s, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {n_layers_sample} of {w.L} layers of one batch-1 step (fp64 C oracle, OpenMP over "
+                       f"output rows); compute time {t_compute:.1f} s, scaled by {w.L}/{n_layers_sample}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-batch8", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=16, help="layers in the CPU-oracle sample")
+    ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the workload's 92)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the decode kernel runs on a single MI355X and this build has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    import moe_layer_stack_amd as mk
+    from moe_layer_stack_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    import synth
+    from synth.stack import DeviceStack
+    from synth.workloads import ATTN92_B8
+    if not os.path.exists(synth.LIB):
+        synth.build()
+    need = args.warmup + args.steps
+    n_seq = 1 if args.no_batch8 else 8
+    w8 = ATTN92_B8.with_(cap_extra=max(64, need + 8), M=n_seq)
+    t0 = time.perf_counter()
+    def prog(l):
+        if l % 16 == 0:
+            torch.cuda.synchronize()
+            log(f"filling layer {l} ({time.perf_counter() - t0:.0f} s)")
+    st = DeviceStack(w8, n_layers=args.layers, progress=prog)
+    torch.cuda.synchronize()
+    log(f"stack: {st.L} layers, {sum(t.numel() * t.element_size() for ly in st.layers for t in ly.values() if t is not None) / 1e9:.1f} GB "
+        f"weights + {2 * st.kc.numel() * 2 / 1e9:.1f} GB KV, built in {time.perf_counter() - t0:.1f} s")
+    w1 = w8.with_(M=1)
+    b1 = run_leg(torch, mk, st, w1, 1, 1, args.steps, args.warmup, trace_union=False)
+    log(f"batch 1: {b1['ms_per_step']:.3f} ms/step, {b1['tok_s']:.1f} tok/s, {b1['achieved_gbps']:.0f} GB/s "
+        f"({100 * b1['frac']:.1f}% of peak)")
+    b8 = None
+    if not args.no_batch8:
+        b8 = run_leg(torch, mk, st, w8, 8, 1, args.steps, args.warmup, trace_union=True)
+        log(f"batch 8: {b8['ms_per_step']:.3f} ms/step, {b8['tok_s']:.1f} tok/s, {b8['achieved_gbps']:.0f} GB/s "
+            f"({100 * b8['frac']:.1f}% of peak), union {b8['union_mean']:.1f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        cpu = cpu_baseline(torch, st, w1, min(args.cpu_layers, st.L))
+        log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads ({time.perf_counter() - t0:.1f} s)")
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic_attn92_b1.json")
+    if os.path.exists(tf):
+        try:
+            rec = json.load(open(tf))
+            if rec.get("source_hash") == source_hash():
+                traffic = rec.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    out = {
+        "metric": METRIC,
+        "value": round(b1["tok_s"], 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(b1["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "attn92_b1", "layers": st.L, "d_model": w1.d, "experts": w1.E, "top_k": w1.k,
+                   "shared_experts": w1.n_shared, "d_ff": w1.F, "q_heads": w1.H, "kv_heads": w1.G,
+                   "head_dim": w1.hd, "kv_past_positions": w1.past, "batch": 1, "weights_dtype": "bf16",
+                   "accumulate": "f32"},
+        "roofline": {"bound": "hbm", "achieved": round(b1["achieved_gbps"], 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(b1["frac"], 4), "traffic": traffic,
+                     "bytes_per_launch": b1["bytes_per_step"]},
+        "cpu_baseline": cpu,
+        "batch1": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b1.items()},
+        "batch8": None if b8 is None else {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b8.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

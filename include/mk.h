@@ -160,6 +160,14 @@ int mk_sync(mk_handle* h, void* stream);
  * weights, in top-k order), logits [L][M][E] fp32 (after bias). */
 int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits);
 
+/* Per-phase timestamps for profiling (NULL turns it off).  stamps is a
+ * device buffer of int64 [n_cu][2 * (barriers_per_step + 1)]: workgroup c
+ * writes the 100 MHz device realtime counter when each phase starts (after
+ * the preceding grid barrier) and when it ends (before the next barrier);
+ * phase i uses slots 2i and 2i+1.  Phases in order per layer: QKV, ATTN, WO
+ * (attention stacks), RS, RG, DOWN. */
+int mk_set_timing(mk_handle* h, int64_t* stamps);
+
 /* Launch geometry and workspace size of a handle. */
 int mk_get_info(const mk_handle* h, mk_info* info);
 

@@ -11,15 +11,18 @@ constexpr int kThreads = 256;           // 4 waves of 64 lanes: one wave per SIM
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = 8192;        // weight tile streamed through the LDS ring
 constexpr int kChunk = 1024;            // one global_load_lds: 64 lanes x 16 B
-constexpr int kMaxRows = 64;            // M
+constexpr int kRing = 12;               // ring slots (tiles in flight per CU)
+constexpr int kMaxRows = 8;             // M
 constexpr int kMaxExperts = 64;         // E (one lane per expert in top-k)
 constexpr int kMaxTopK = 8;
 constexpr int kMaxShared = 4;
 constexpr int kMaxQ = 32;               // query vectors per attention task
 constexpr int kAttnTile = 32;           // positions per KV tile (hd = 128 bf16 -> 8 KB)
 constexpr int kLdsTotal = 160 * 1024;
-constexpr int kPartBytes = 8 * 1024;
+constexpr int kPartBytes = 16 * 1024;
 constexpr int kMiscBytes = 8 * 1024;
+constexpr int kXsBytes = kLdsTotal - kRing * kTileBytes - kPartBytes - kMiscBytes;  // 40 KiB
+constexpr int kPartStride = 132;        // floats per attention partial: m, l, pad, pad, acc[128]
 
 // device error flag bits
 enum : unsigned { kErrTimeout = 1u, kErrPosition = 2u, kErrDupPosition = 4u };
@@ -47,11 +50,12 @@ struct DevLayer {
 struct ActLayout {
   size_t h1;      // [M][d]
   size_t qkv;     // [M][(H+2G)*hd]   raw projections (RoPE applied by the reader)
-  size_t part;    // [n_seq][G][S][Q][hd+2]  attention partials (m, l, acc)
+  size_t part;    // [n_seq][G][S][Q][kPartStride]  attention partials (m, l, -, -, acc[hd])
   size_t o;       // [M][H*hd]
   size_t logits;  // [M][E]
   size_t a_s;     // [M][n_shared][F]  shared SwiGLU activations
   size_t a;       // [M][k][F]         routed SwiGLU activations (slot = top-k rank)
+  size_t y_s;     // [M][d]            shared-expert down projection
   size_t h2;      // [M][d]            layer output (next layer's input)
   size_t stride;  // bytes per layer
 };
@@ -92,6 +96,7 @@ struct KParams {
   ActLayout al;
   unsigned* sync;            // SyncLayout
   unsigned* attn_cnt;        // [L][n_seq][G]
+  long long* stamps;         // [n_cu][2*(barriers+1)] or null
   int* t_ids;
   float* t_w;
   float* t_logits;

@@ -58,6 +58,7 @@ struct mk_handle {
   int32_t* t_ids = nullptr;
   float* t_w = nullptr;
   float* t_logits = nullptr;
+  int64_t* stamps = nullptr;
 };
 
 namespace {
@@ -163,18 +164,9 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
     h->n_splits = s;
   }
   h->barriers = c.n_layers * (c.has_attn ? 6 : 3) - 1;
-  // LDS: x region sized for the largest fp32 activation block (capped), ring gets the rest
-  long long xneed = (long long)M * c.d_model;
-  if (c.has_attn && (long long)M * H * hd > xneed) xneed = (long long)M * H * hd;
-  if ((long long)M * (c.n_shared + c.top_k) * c.d_ff > xneed) xneed = (long long)M * (c.n_shared + c.top_k) * c.d_ff;
-  xneed *= 4;
-  const long long xattn = (long long)(mk::kMaxQ * 128 + mk::kMaxQ * 32) * 4;
-  if (xneed < xattn) xneed = xattn;
-  if (xneed > 64 * 1024) xneed = 64 * 1024;
-  h->x_bytes = (int)((xneed + 1023) / 1024 * 1024);
-  int ring = (mk::kLdsTotal - h->x_bytes - mk::kPartBytes - mk::kMiscBytes) / mk::kTileBytes;
-  if (ring > 24) ring = 24;
-  h->ring_tiles = ring;
+  // LDS: fixed carve-up (ring, x staging, per-row partial sums, misc)
+  h->x_bytes = mk::kXsBytes;
+  h->ring_tiles = mk::kRing;
   // activation scratch per layer
   const int E = c.n_experts, k = c.top_k, S = c.n_shared, F = c.d_ff, d = c.d_model;
   const int Q = c.has_attn ? c.rows_per_seq * (H / G) : 0;
@@ -187,18 +179,12 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   };
   al.h1 = take((size_t)M * d * 4);
   al.qkv = take((size_t)M * (H + 2 * G) * hd * 4);
-  al.part = take((size_t)n_seq * G * h->n_splits * Q * (hd + 2) * 4);
+  al.part = take((size_t)n_seq * G * h->n_splits * Q * mk::kPartStride * 4);
   al.o = take((size_t)M * H * hd * 4);
   al.logits = take((size_t)M * E * 4);
   al.a_s = take((size_t)M * S * F * 4);
-  al.a = off;  // must directly follow a_s (phase DOWN reads both as one block)
-  off = al.a + (size_t)M * k * F * 4;
-  if (S > 0 && al.a != al.a_s + (size_t)M * S * F * 4) {
-    // a_s size is a multiple of 256 when F*4 is, which validate() guarantees
-    delete h;
-    return fail(MK_ERR_UNSUPPORTED, "internal layout error");
-  }
-  off = align256(off);
+  al.a = take((size_t)M * k * F * 4);
+  al.y_s = take((size_t)M * d * 4);
   al.h2 = take((size_t)M * d * 4);
   al.stride = align256(off);
   h->al = al;
@@ -252,6 +238,12 @@ int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits) {
   h->t_ids = ids;
   h->t_w = w;
   h->t_logits = logits;
+  return MK_OK;
+}
+
+int mk_set_timing(mk_handle* h, int64_t* stamps) {
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  h->stamps = stamps;
   return MK_OK;
 }
 
@@ -313,6 +305,7 @@ int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* position
   p.sync = h->d_sync;
   p.attn_cnt = h->d_attn_cnt;
   p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
+  p.stamps = reinterpret_cast<long long*>(h->stamps);
   int e = mk_launch_kernel(&p, stream);
   if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
   if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));

@@ -26,7 +26,7 @@ class DeviceStack:
     n_layers overrides the workload's layer count (parity tests on a prefix
     of a deep stack: layer l is the same data whatever n_layers is)."""
 
-    def __init__(self, w: Workload, n_layers=None, device="cuda", fill=True, hidden_seed=None):
+    def __init__(self, w: Workload, n_layers=None, device="cuda", fill=True, progress=None):
         torch = _torch()
         self.w = w
         self.L = w.L if n_layers is None else n_layers
@@ -60,15 +60,18 @@ class DeviceStack:
         else:
             self.kc = self.vc = None
         if fill:
-            self.fill()
+            self.fill(progress)
 
     # ------------------------------------------------------------ generation
     def _dt(self):
         return BF16 if self.w.dtype == BF16 else F32
 
-    def fill(self):
+    def fill(self, progress=None):
+        """progress(l) is called after each layer's tensors are enqueued."""
         w, dt, seed = self.w, self._dt(), self.w.weight_seed
         for l, t in enumerate(self.layers):
+            if progress is not None:
+                progress(l)
             device_uniform(t["g2"].data_ptr(), w.d, dt, seed, stream_id(l, K_G2), 0.9, 1.1)
             device_normal(t["wr"].data_ptr(), t["wr"].numel(), dt, seed, stream_id(l, K_WR), 0.0, w.weight_std)
             if t["br"] is not None:

@@ -41,6 +41,7 @@ class Workload:
     weight_seed: int = 0
     input_seed: int = 0
     steps: int = 1
+    cap_extra: int = 64       # KV capacity beyond past + rows_per_seq (room for more steps)
     rms_eps: float = 1e-6
     weight_std: float = 0.02
     bias_std: float = 0.5
@@ -52,7 +53,7 @@ class Workload:
     @property
     def capacity(self) -> int:
         # room for the step's new rows plus a few more steps of growth
-        return self.past + self.rows_per_seq + 64 if self.has_attn else 0
+        return self.past + self.rows_per_seq + self.cap_extra if self.has_attn else 0
 
     def positions(self, step: int = 0):
         """Row r of sequence s sits at past + step*rows_per_seq + (r % rows_per_seq)."""
