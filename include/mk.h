@@ -161,10 +161,11 @@ int mk_sync(mk_handle* h, void* stream);
 int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits);
 
 /* Per-phase timestamps for profiling (NULL turns it off).  stamps is a
- * device buffer of int64 [n_cu][2 * (barriers_per_step + 1)]: workgroup c
- * writes the 100 MHz device realtime counter when each phase starts (after
- * the preceding grid barrier) and when it ends (before the next barrier);
- * phase i uses slots 2i and 2i+1.  Phases in order per layer: QKV, ATTN, WO
+ * device buffer of int64 [n_cu][4 * (barriers_per_step + 1)]: workgroup c
+ * writes the 100 MHz device realtime counter at four points of each phase
+ * i, into slots 4i .. 4i+3: the phase start (after the preceding grid
+ * barrier), the start and the end of its weight-tile loop, and the phase end
+ * (before the next barrier).  Phases in order per layer: QKV, ATTN, WO
  * (attention stacks), RS, RG, DOWN. */
 int mk_set_timing(mk_handle* h, int64_t* stamps);
 

@@ -96,7 +96,7 @@ struct KParams {
   ActLayout al;
   unsigned* sync;            // SyncLayout
   unsigned* attn_cnt;        // [L][n_seq][G]
-  long long* stamps;         // [n_cu][2*(barriers+1)] or null
+  long long* stamps;         // [n_cu][4*(barriers+1)] or null
   int* t_ids;
   float* t_w;
   float* t_logits;

@@ -94,34 +94,53 @@ __device__ __forceinline__ void st_dev_u(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 16 bytes per lane, global -> LDS at (wave-uniform base + lane*16), nontemporal
+// 16 bytes per lane, global -> LDS at (wave-uniform base + lane*16),
+// nontemporal.  Issued from inline assembly on purpose: the compiler's
+// wait-count pass cannot tell LDS DMA destinations apart from other LDS data,
+// so for a DMA it can see it puts a full vector-memory drain in front of
+// every later LDS access, which would serialise the ring.  Here the ring's
+// waits are all explicit (wait_tiles_ahead / wait_all), and every wait is a
+// compiler memory barrier so no LDS read of a slot moves above it.
 __device__ __forceinline__ void g2l(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 2);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_wave_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off nt"
+      :
+      : "v"(g), "s"(m0)
+      : "memory", "m0");
 }
 
-// s_waitcnt encodings (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14
-#define MK_VMCNT(n) (((n)&15) | ((((n) >> 4) & 3) << 14) | 0x70 | 0xF00)
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// s_waitcnt with compiler memory-barrier semantics
+#define MK_WAIT_ASM(text) asm volatile(text ::: "memory")
+__device__ __forceinline__ void wait_all() { MK_WAIT_ASM("s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)"); }
+// Wait for everything, through the builtin the compiler's wait-count pass
+// understands: called before each tile loop, it leaves no compiler-visible
+// load pending, so the pass puts no waits inside the loop (which, not seeing
+// the ring's loads, would otherwise drain the ring every tile).
+__device__ __forceinline__ void settle() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void wait_lgkm0() { MK_WAIT_ASM("s_waitcnt lgkmcnt(0)"); }
 // wait until at most 2*ahead vector-memory operations of this wave are outstanding
 __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
   static_assert(2 * (kRing - 1) <= 63, "vmcnt range");
   if (ahead >= kRing - 1) {
-    __builtin_amdgcn_s_waitcnt(MK_VMCNT(2 * (kRing - 1)));
+    MK_WAIT_ASM("s_waitcnt vmcnt(22)");
     return;
   }
   switch (ahead) {
-#define MK_CASE(k) \
-  case k:          \
-    __builtin_amdgcn_s_waitcnt(MK_VMCNT(2 * k)); \
+#define MK_CASE(k, n)          \
+  case k:                      \
+    MK_WAIT_ASM("s_waitcnt vmcnt(" #n ")"); \
     break;
-    MK_CASE(1) MK_CASE(2) MK_CASE(3) MK_CASE(4) MK_CASE(5) MK_CASE(6) MK_CASE(7) MK_CASE(8) MK_CASE(9) MK_CASE(10)
+    MK_CASE(1, 2) MK_CASE(2, 4) MK_CASE(3, 6) MK_CASE(4, 8) MK_CASE(5, 10) MK_CASE(6, 12) MK_CASE(7, 14)
+    MK_CASE(8, 16) MK_CASE(9, 18) MK_CASE(10, 20)
 #undef MK_CASE
     default:
-      __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
+      MK_WAIT_ASM("s_waitcnt vmcnt(0)");
   }
 }
-static_assert(kRing - 2 <= 10, "extend wait_tiles_ahead");
+static_assert(kRing == 12, "wait_tiles_ahead is written for a ring of 12 tiles");
 
 __device__ __forceinline__ int ilog2(int x) { return 31 - __builtin_clz(x); }
 
@@ -138,6 +157,9 @@ struct Misc {
   int last;
   int epoch;
   float rinv[kMaxRows];
+  float ssq[kWaves * kMaxRows];
+  unsigned umask[kMaxExperts];                 // union expert u: rows routed to it
+  signed char uslot[kMaxExperts * kMaxRows];   // [u][t]: top-k slot of expert u in row t, or -1
   unsigned char used[kMaxExperts];
   float rope[kMaxRows * 64 * 2];  // (cos, sin) per row and frequency (head_dim 128)
 };
@@ -199,6 +221,14 @@ __device__ __forceinline__ bool grid_sync(const KParams& p, Smem sm, unsigned ta
 
 // ------------------------------------------------------------------ layer data access
 
+// The weight-pointer table is written by the host before the launch and never
+// by the kernel, so it is read through the constant address space: uniform
+// reads become scalar loads, which count on lgkmcnt and do not wait behind
+// the ring's outstanding vector-memory loads.
+typedef const __attribute__((address_space(4))) DevLayer* ConstLayers;
+__device__ __forceinline__ ConstLayers layer_tab(const KParams& p) { return (ConstLayers)p.layers; }
+
+
 __device__ __forceinline__ const float* act_f(const KParams& p, int l, size_t off) {
   return reinterpret_cast<const float*>(p.act + (size_t)l * p.al.stride + off);
 }
@@ -236,6 +266,7 @@ struct Plan {
   int lo2;           // first unit of the second segment
   int lrb2, rpt2;    // second segment geometry (RS, RG)
   int fb_per;        // f-blocks per expert in the second segment
+  int nj;            // RG: shared-down units; DOWN: j-blocks per expert
   int a0, a1;        // QKV: nq, nk; ATTN: p_lo, p_hi; RS: E; RG, DOWN: unused
   int d, F, S, U;
   const char* b0;
@@ -276,8 +307,8 @@ __device__ __forceinline__ TileSrc plan_tile(const Plan& P, int i, const Misc* m
       return TileSrc{((k & 1) ? P.b2 : P.b1) + (((size_t)sx * P.F + (size_t)fb * P.rpt) << P.lrb), kTileBytes};
     }
     case PK_RG: {
-      if (i < P.n1) {  // shared down: unit = j-block, S tiles per unit
-        const int unit = P.lo + i / P.S, s = i % P.S;
+      if (i < P.n1) {  // shared down, expert-major: tile = s * nj + unit
+        const int s = i / P.nj, unit = P.lo + i % P.nj;
         return TileSrc{P.b0 + (((size_t)s * P.d + (size_t)unit * P.rpt) << P.lrb), kTileBytes};
       }
       const int k = i - P.n1;
@@ -285,8 +316,8 @@ __device__ __forceinline__ TileSrc plan_tile(const Plan& P, int i, const Misc* m
       const int e = ms->uni[pj / P.fb_per], fb = pj % P.fb_per;
       return TileSrc{((k & 1) ? P.b2 : P.b1) + (((size_t)e * P.F + (size_t)fb * P.rpt2) << P.lrb2), kTileBytes};
     }
-    case PK_DOWN: {
-      const int jb = P.lo + i / P.U, u = i % P.U;
+    case PK_DOWN: {  // expert-major: tile = u * nj + (jb - lo)
+      const int u = i / P.nj, jb = P.lo + i % P.nj;
       return TileSrc{P.b0 + (((size_t)ms->uni[u] * P.d + (size_t)jb * P.rpt) << P.lrb), kTileBytes};
     }
     default:
@@ -296,7 +327,7 @@ __device__ __forceinline__ TileSrc plan_tile(const Plan& P, int i, const Misc* m
 
 template <typename WT>
 __device__ __forceinline__ Plan plan_qkv(const KParams& p, int l) {
-  const DevLayer& Ly = p.layers[l];
+  const auto& Ly = layer_tab(p)[l];
   Plan P{};
   P.kind = PK_QKV;
   P.lrb = ilog2(p.d * (int)sizeof(WT));
@@ -346,7 +377,7 @@ __device__ __forceinline__ Plan plan_wo(const KParams& p, int l) {
   my_range(p.d / P.rpt, p.n_cu, lo, hi);
   P.lo = lo;
   P.n = hi - lo;
-  P.b0 = (const char*)p.layers[l].wo;
+  P.b0 = (const char*)layer_tab(p)[l].wo;
   return P;
 }
 
@@ -354,7 +385,7 @@ __device__ __forceinline__ Plan plan_wo(const KParams& p, int l) {
 // split by cumulative weight so that a pair never straddles two CUs
 template <typename WT>
 __device__ __forceinline__ Plan plan_rs(const KParams& p, int l) {
-  const DevLayer& Ly = p.layers[l];
+  const auto& Ly = layer_tab(p)[l];
   Plan P{};
   P.kind = PK_RS;
   P.lrb = ilog2(p.d * (int)sizeof(WT));
@@ -383,7 +414,7 @@ __device__ __forceinline__ Plan plan_rs(const KParams& p, int l) {
 // routing is known (routed = true), the routed gate/up pairs
 template <typename WT>
 __device__ __forceinline__ Plan plan_rg(const KParams& p, const Misc* ms, int l, bool routed) {
-  const DevLayer& Ly = p.layers[l];
+  const auto& Ly = layer_tab(p)[l];
   Plan P{};
   P.kind = PK_RG;
   P.lrb = ilog2(p.F * (int)sizeof(WT));
@@ -396,6 +427,7 @@ __device__ __forceinline__ Plan plan_rg(const KParams& p, const Misc* ms, int l,
   int lo, hi;
   my_range(p.S > 0 ? p.d / P.rpt : 0, p.n_cu, lo, hi);
   P.lo = lo;
+  P.nj = hi - lo;
   P.n1 = (hi - lo) * p.S;
   P.fb_per = p.F / P.rpt2;
   P.n = P.n1;
@@ -422,18 +454,52 @@ __device__ __forceinline__ Plan plan_down(const KParams& p, const Misc* ms, int 
   int lo, hi;
   my_range(p.d / P.rpt, p.n_cu, lo, hi);
   P.lo = lo;
+  P.nj = hi - lo;
   P.n = (hi - lo) * P.U;
-  P.b0 = (const char*)p.layers[l].w_down;
+  P.b0 = (const char*)layer_tab(p)[l].w_down;
   return P;
 }
 
 // ------------------------------------------------------------------ tile stream
 
-__device__ __forceinline__ void issue_quarter(TileSrc t, char* slot, int wave, int lane) {
+// Tile addresses of one plan for 64 consecutive tiles, one per lane (lane j
+// holds tile w0 + j), evaluated in parallel by plan_tile; issuing a tile then
+// costs two v_readlane.  hi keeps the upper address bits in 0..26 and
+// (kTileBytes - valid) / 256 in bits 27..31.
+struct Win {
+  unsigned lo, hi;
+  int w0;
+};
+constexpr int kNoWin = -(1 << 24);
+__device__ __forceinline__ Win build_win(const Plan& P, int w0, const Misc* ms, int lane) {
+  const int j = w0 + lane;
+  TileSrc t{nullptr, kTileBytes};
+  if (j < P.n) t = plan_tile(P, j, ms);
+  const unsigned long long a = (unsigned long long)(uintptr_t)t.g;
+  Win w;
+  w.lo = (unsigned)a;
+  w.hi = (unsigned)(a >> 32) | ((unsigned)((kTileBytes - t.valid) >> 8) << 27);
+  w.w0 = w0;
+  return w;
+}
+
+// issue this wave's quarter of tile j (of the window's plan) into `slot`
+__device__ __forceinline__ void issue_tile(const Win& w, int j, char* slot, int wave, int lane) {
+  const int idx = j - w.w0;
+  const unsigned lo = __builtin_amdgcn_readlane(w.lo, idx);
+  const unsigned hi = __builtin_amdgcn_readlane(w.hi, idx);
+  const char* g = reinterpret_cast<const char*>(((unsigned long long)(hi & 0x07ffffffu) << 32) | lo);
+  const int valid = kTileBytes - (int)((hi >> 27) << 8);
   const int off0 = wave * 2048 + lane * 16;
   const int off1 = off0 + 1024;
-  g2l(t.g + (off0 < t.valid ? off0 : 0), slot + wave * 2048);
-  g2l(t.g + (off1 < t.valid ? off1 : 0), slot + wave * 2048 + 1024);
+  g2l(g + (off0 < valid ? off0 : 0), slot + wave * 2048);
+  g2l(g + (off1 < valid ? off1 : 0), slot + wave * 2048 + 1024);
+}
+
+// Copy `bytes` (a multiple of 1 KiB) from global memory to LDS by DMA, 1 KiB
+// per wave instruction.  Completion needs wait_all() and a workgroup sync.
+__device__ __forceinline__ void dma_to_lds(char* lds, const char* g, int bytes, int wave, int lane) {
+  for (int c = wave * 1024; c < bytes; c += kWaves * 1024) g2l(g + c + lane * 16, lds + c);
 }
 
 // The stream of one phase followed by the next: tile j < cur.n is the
@@ -443,6 +509,11 @@ __device__ __forceinline__ void issue_quarter(TileSrc t, char* slot, int wave, i
 struct Stream {
   int slot0;
   int issued;
+  long long* ts;  // this phase's 4 timestamp slots, or null
+  Win wc, wn;     // address windows of the current and the next plan
+  __device__ __forceinline__ void mark(int k) const {
+    if (ts && threadIdx.x == 0) ts[k] = wall_clock64();
+  }
   __device__ __forceinline__ char* slot(Smem sm, int j) const {
     return sm.ring + (size_t)((slot0 + j) % kRing) * kTileBytes;
   }
@@ -452,18 +523,27 @@ struct Stream {
     const int limit = min(consumed + kRing, cur.n + nxt.n);
     if (issued >= limit) return;
     wait_lgkm0();  // this wave's reads of the slots being refilled are done
-    const Misc* ms = sm.misc;
     for (; issued < limit; ++issued) {
-      const TileSrc t = issued < cur.n ? plan_tile(cur, issued, ms) : plan_tile(nxt, issued - cur.n, ms);
-      issue_quarter(t, slot(sm, issued), wave, lane);
+      char* s = slot(sm, issued);
+      if (issued < cur.n) {
+        if ((unsigned)(issued - wc.w0) >= 64u) wc = build_win(cur, issued, sm.misc, lane);
+        issue_tile(wc, issued, s, wave, lane);
+      } else {
+        const int j = issued - cur.n;
+        if ((unsigned)(j - wn.w0) >= 64u) wn = build_win(nxt, j, sm.misc, lane);
+        issue_tile(wn, j, s, wave, lane);
+      }
     }
   }
   // wait until tile i of cur has landed (this wave's quarter)
   __device__ __forceinline__ void wait(int i) const { wait_tiles_ahead(issued - 1 - i); }
-  // hand over to the next phase: its first tiles are already issued
+  // hand over to the next phase: its first tiles are already issued.  The
+  // next phase may re-plan (same leading tiles), so both windows are rebuilt.
   __device__ __forceinline__ void advance(const Plan& cur) {
     slot0 = (slot0 + cur.n) % kRing;
     issued -= cur.n;
+    wc.w0 = kNoWin;
+    wn.w0 = kNoWin;
   }
 };
 
@@ -515,38 +595,134 @@ __device__ __forceinline__ void load_x(XRegs<WT, MT>& xr, const float* src, int 
   }
 }
 
-// One wave's quarter of a weight tile against the x registers.  For chunk c
-// and token t the dot product of this wave's part of the row is summed over
-// the wave and written (scaled by tw[t]; added when accum) to
-// part_wave[c*MT + t].  tmask selects the tokens that take part.
+// load_x for an RMSNorm'd input: x = h * gain, and misc->rinv[t] =
+// 1/sqrt(mean(h_t^2) + eps) from the same loads.  Each element of a row is
+// loaded by rpt = kTileBytes >> lrb lanes of the workgroup (one per row of a
+// tile), so the workgroup's sum of squares is rpt times the row's.  rinv is
+// ready after the workgroup's next synchronisation.
 template <typename WT, int MT>
-__device__ __forceinline__ void gemv_quarter(const char* slot, const XRegs<WT, MT>& xr, unsigned tmask,
-                                             const float (&tw)[MT], float* part_wave, bool accum, int wave,
-                                             int lane) {
+__device__ __forceinline__ void load_x_norm(XRegs<WT, MT>& xr, Smem sm, const float* src, int ld, const WT* gam,
+                                            int M, int d, float eps, int wave, int lane, int lrb) {
   constexpr int EPL = XRegs<WT, MT>::EPL;
-  float acc[2 * MT];
+  float ss[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) ss[t] = 0.f;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const uint4 wv = *reinterpret_cast<const uint4*>(slot + wave * 2048 + c * 1024 + lane * 16);
-    float w[EPL];
-    unpack16<WT>(wv, w);
+    const int k0 = lane_k0<WT>(wave, lane, c, lrb);
+    float g[EPL];
+    unpack16<WT>(*reinterpret_cast<const uint4*>(gam + k0), g);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      float s = 0.f;
-      if (tmask & (1u << t)) {
+      if (t < M) {
+        const float* s = src + (size_t)t * ld + k0;
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) s = fmaf(w[j], xr.v[t][c][j], s);
-        s *= tw[t];
+        for (int j = 0; j < EPL; j += 4) {
+          const float4 a = *reinterpret_cast<const float4*>(s + j);
+          ss[t] = fmaf(a.x, a.x, fmaf(a.y, a.y, fmaf(a.z, a.z, fmaf(a.w, a.w, ss[t]))));
+          xr.v[t][c][j] = a.x * g[j]; xr.v[t][c][j + 1] = a.y * g[j + 1];
+          xr.v[t][c][j + 2] = a.z * g[j + 2]; xr.v[t][c][j + 3] = a.w * g[j + 3];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) xr.v[t][c][j] = 0.f;
       }
-      acc[c * MT + t] = s;
     }
   }
-  const float r = xreduce<2 * MT>(acc, lane);
-  if (xreduce_writer<2 * MT>(lane)) {
-    const int idx = xreduce_index<2 * MT>(lane);
-    if (accum) part_wave[idx] += r;
-    else part_wave[idx] = r;
+  const float r = xreduce<MT>(ss, lane);
+  if (xreduce_writer<MT>(lane)) {
+    const int t = xreduce_index<MT>(lane);
+    if (t < M) sm.misc->ssq[wave * kMaxRows + t] = r;
   }
+  __syncthreads();
+  if ((int)threadIdx.x < M) {
+    const int t = threadIdx.x;
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += sm.misc->ssq[w * kMaxRows + t];
+    const float rpt = (float)(kTileBytes >> lrb);
+    sm.misc->rinv[t] = 1.0f / sqrtf(tot / (rpt * (float)d) + eps);
+  }
+}
+
+// Tiles consumed per step of the GEMV loop: one cross-lane reduction serves
+// the whole group (2 * G * MT values per lane).
+template <int MT>
+struct GroupOf {
+  static constexpr int G = MT == 1 ? 4 : 1;
+};
+
+// This wave's quarter of g <= G consecutive tiles (ring slots of tiles i ..
+// i+g-1) against the x registers.  For tile i+u, chunk c and token t the dot
+// product over the wave is scaled by tw[t] and stored (added when accum) at
+// part[(blk0 + u) * kWaves*2*MT + (wave*2 + c)*MT + t].  Tokens outside tmask
+// contribute zero.
+template <typename WT, int MT>
+__device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int g, const XRegs<WT, MT>& xr,
+                                           unsigned tmask, const float (&tw)[MT], int blk0, bool accum, int wave,
+                                           int lane) {
+  constexpr int G = GroupOf<MT>::G;
+  constexpr int EPL = XRegs<WT, MT>::EPL;
+  constexpr int NV = G * 2 * MT;
+  uint4 wv[G][2];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    if (u < g) {
+      const char* sl = st.slot(sm, i + u) + wave * 2048 + lane * 16;
+      wv[u][0] = *reinterpret_cast<const uint4*>(sl);
+      wv[u][1] = *reinterpret_cast<const uint4*>(sl + 1024);
+    }
+  }
+  float acc[NV];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float w[EPL];
+      unpack16<WT>(wv[u][c], w);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        float s0 = 0.f, s1 = 0.f;
+        if (u < g && (tmask & (1u << t))) {
+#pragma unroll
+          for (int j = 0; j < EPL; j += 2) {
+            s0 = fmaf(w[j], xr.v[t][c][j], s0);
+            s1 = fmaf(w[j + 1], xr.v[t][c][j + 1], s1);
+          }
+        }
+        acc[(u * 2 + c) * MT + t] = (s0 + s1) * tw[t];
+      }
+    }
+  }
+  const float r = xreduce<NV>(acc, lane);
+  if (xreduce_writer<NV>(lane)) {
+    const int idx = xreduce_index<NV>(lane);
+    const int u = idx / (2 * MT), c = (idx / MT) & 1, t = idx % MT;
+    if (u < g) {
+      float* dst = sm.part + (size_t)(blk0 + u) * (kWaves * 2 * MT) + (wave * 2 + c) * MT + t;
+      if (accum) *dst += r;
+      else *dst = r;
+    }
+  }
+}
+
+// A run of tiles that share x registers, token mask and weights, with
+// consecutive part blocks starting at blk0; the loop calls the phase's
+// epilogue after the run when round_end is set.
+template <int MT>
+struct Seg {
+  int end;
+  int blk0;
+  bool accum;
+  bool round_end;
+  unsigned tmask;
+  float tw[MT];
+};
+template <int MT>
+__device__ __forceinline__ void seg_all(Seg<MT>& sg, int M) {
+  sg.tmask = (1u << M) - 1u;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) sg.tw[t] = 1.f;
 }
 
 // part block layout: [wave][c][MT]; the row of (wave, c) in a tile of
@@ -563,59 +739,69 @@ __device__ __forceinline__ float part_row(const float* part, int block, int q, i
   return s;
 }
 
-// Consume the tiles of GEMV phase `cur`.  pre(i, tmask, tw, accum) may
-// refresh the x registers and gives tile i's token mask, token weights and
-// whether it accumulates into its part block; block(i) gives the block;
-// is_end(i) closes a round, after which round_end(first, last) runs with all
-// waves synchronised.  The stream keeps issuing `nxt`'s tiles meanwhile.
-template <typename WT, int MT, class PreFn, class BlockFn, class IsEnd, class RoundEnd>
+// Consume the tiles of GEMV phase `cur` in groups.  seg(i, sg) describes the
+// run starting at tile i (and may reload the x registers); after a run with
+// round_end set, all waves synchronise and epi(first, last) runs over the
+// round's tiles.  The stream keeps issuing `nxt`'s tiles meanwhile.
+template <typename WT, int MT, class SegFn, class EpiFn>
 __device__ __forceinline__ void run_gemv(Smem sm, Stream& st, const Plan& cur, const Plan& nxt, XRegs<WT, MT>& xr,
-                                         PreFn pre, BlockFn block, IsEnd is_end, RoundEnd round_end) {
+                                         SegFn seg, EpiFn epi) {
+  constexpr int G = GroupOf<MT>::G;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  st.mark(1);
+  settle();
   st.fill(sm, cur, nxt, 0, wave, lane);
   int round_first = 0;
-  for (int i = 0; i < cur.n; ++i) {
-    unsigned tmask;
-    float tw[MT];
-    bool accum;
-    pre(i, tmask, tw, accum);
-    st.wait(i);
-    gemv_quarter<WT, MT>(st.slot(sm, i), xr, tmask, tw,
-                         sm.part + (size_t)block(i) * (kWaves * 2 * MT) + wave * 2 * MT, accum, wave, lane);
-    st.fill(sm, cur, nxt, i + 1, wave, lane);
-    if (is_end(i)) {
-      __syncthreads();
-      round_end(round_first, i);
-      __syncthreads();
-      round_first = i + 1;
+  for (int i = 0; i < cur.n;) {
+    Seg<MT> sg;
+    seg(i, sg);
+    for (int j = i; j < sg.end; j += G) {
+      const int g = min(G, sg.end - j);
+      st.wait(j + g - 1);
+      gemv_group<WT, MT>(sm, st, j, g, xr, sg.tmask, sg.tw, sg.blk0 + (j - i), sg.accum, wave, lane);
+      st.fill(sm, cur, nxt, j + g, wave, lane);
     }
+    if (sg.round_end) {
+      __syncthreads();
+      epi(round_first, sg.end - 1);
+      __syncthreads();
+      round_first = sg.end;
+    }
+    i = sg.end;
   }
+  st.mark(2);
 }
 
+// The part region holds the GEMV accumulators (kPartAcc floats) followed by
+// the residual slice (kResFloats) an epilogue adds: epilogues read it from
+// LDS because a global load there would wait behind the ring's loads.
+constexpr int kPartAcc = 3072;
+constexpr int kResFloats = kPartBytes / 4 - kPartAcc;
+__device__ __forceinline__ float* res_slice(Smem sm) { return sm.part + kPartAcc; }
 __device__ __forceinline__ void zero_part(Smem sm) {
-  for (int i = threadIdx.x; i < kPartBytes / 4; i += kThreads) sm.part[i] = 0.f;
+  for (int i = threadIdx.x; i < kPartAcc; i += kThreads) sm.part[i] = 0.f;
 }
-
-// 1 / sqrt(mean(h^2) + eps) per row, into misc->rinv
-__device__ __forceinline__ void row_rinv(Smem sm, const float* h, int M, int d, float eps) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = wave; t < M; t += kWaves) {
-    float s = 0.f;
-    for (int i = lane * 4; i < d; i += 256) {
-      const float4 v = *reinterpret_cast<const float4*>(h + (size_t)t * d + i);
-      s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    s = sum_rows(sum_row16(s));
-    if (lane == 0) sm.misc->rinv[t] = 1.0f / sqrtf(s / (float)d + eps);
+// res[t*ncol + c] = a[t*ld + c0 + c] (+ b[t*ld + c0 + c])
+__device__ __forceinline__ void load_res(Smem sm, const float* a, const float* b, int ld, int c0, int ncol, int M) {
+  float* res = res_slice(sm);
+  for (int it = threadIdx.x; it < ncol * M; it += kThreads) {
+    const int t = it / ncol, c = it - t * ncol;
+    float v = a[(size_t)t * ld + c0 + c];
+    if (b) v += b[(size_t)t * ld + c0 + c];
+    res[it] = v;
   }
 }
 
+// Runs of the tiles [base, end) in rounds of kRound tiles (one part block
+// per tile, all tokens); i is the first tile of a round.
 template <int MT>
-__device__ __forceinline__ void all_tokens(int M, unsigned& tmask, float (&tw)[MT], bool& accum) {
-  tmask = (1u << M) - 1u;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) tw[t] = 1.f;
-  accum = false;
+__device__ __forceinline__ void seg_rounds(Seg<MT>& sg, int i, int base, int end, int kRound, int M) {
+  const int k = i - base;
+  sg.end = base + min(end - base, (k / kRound + 1) * kRound);
+  sg.blk0 = k % kRound;
+  sg.accum = false;
+  sg.round_end = true;
+  seg_all<MT>(sg, M);
 }
 
 // ------------------------------------------------------------------ phases
@@ -629,16 +815,15 @@ __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stre
   const float* h = layer_in(p, l);
   float* qkv = act_w(p, l, p.al.qkv);
   XRegs<WT, MT> xr;
-  load_x<WT, MT>(xr, h, d, reinterpret_cast<const WT*>(p.layers[l].attn_norm), M, wave, lane, P.lrb);
-  row_rinv(sm, h, M, d, p.eps);
+  load_x_norm<WT, MT>(xr, sm, h, d, reinterpret_cast<const WT*>(layer_tab(p)[l].attn_norm), M, d, p.eps, wave, lane,
+                      P.lrb);
   zero_part(sm);
   __syncthreads();
-  constexpr int kRound = (kPartBytes / 4) / (kWaves * 2 * MT);
+  constexpr int kRound = kPartAcc / (kWaves * 2 * MT);
   const Misc* ms = sm.misc;
   const int rpt = P.rpt, lo = P.lo, lrb = P.lrb, n = P.n;
   run_gemv<WT, MT>(
-      sm, st, P, N, xr, [&](int, unsigned& tm, float (&tw)[MT], bool& ac) { all_tokens<MT>(M, tm, tw, ac); },
-      [](int i) { return i % kRound; }, [=](int i) { return ((i + 1) % kRound) == 0 || i == n - 1; },
+      sm, st, P, N, xr, [&](int i, Seg<MT>& sg) { seg_rounds<MT>(sg, i, 0, n, kRound, M); },
       [&](int first, int last) {
         const int nr = (last - first + 1) * rpt;
         for (int it = threadIdx.x; it < nr * M; it += kThreads) {
@@ -736,6 +921,8 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
     lsum[i] = 0.f;
     qlim[i] = (active && q < Q) ? min(p_hi - 1, ms->pos[seq * rps + q / HG]) : -1;  // last visible position
   }
+  st.mark(1);
+  settle();
   st.fill(sm, P, N, 0, wave, lane);
   for (int i = 0; i < P.n; ++i) {
     st.wait(i);
@@ -799,6 +986,7 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
     }
   }
   st.fill(sm, P, N, P.n, wave, lane);
+  st.mark(2);
   if (!active) return;
   // sum the 4 position groups; lanes 0-15 hold acc for dims d0..d0+7
   float* part = act_w(p, l, p.al.part) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
@@ -874,18 +1062,20 @@ __device__ __forceinline__ void phase_wo(const KParams& p, Smem sm, int l, Strea
   XRegs<WT, MT> xr;
   load_x<WT, MT>(xr, o, K, (const WT*)nullptr, M, wave, lane, P.lrb);
   zero_part(sm);
-  __syncthreads();
-  constexpr int kRound = (kPartBytes / 4) / (kWaves * 2 * MT);
   const int rpt = P.rpt, lo = P.lo, lrb = P.lrb, n = P.n;
+  const int ncol = n * rpt;
+  load_res(sm, h, nullptr, d, lo * rpt, ncol, M);
+  __syncthreads();
+  constexpr int kRound = kPartAcc / (kWaves * 2 * MT);
+  const float* res = res_slice(sm);
   run_gemv<WT, MT>(
-      sm, st, P, N, xr, [&](int, unsigned& tm, float (&tw)[MT], bool& ac) { all_tokens<MT>(M, tm, tw, ac); },
-      [](int i) { return i % kRound; }, [=](int i) { return ((i + 1) % kRound) == 0 || i == n - 1; },
+      sm, st, P, N, xr, [&](int i, Seg<MT>& sg) { seg_rounds<MT>(sg, i, 0, n, kRound, M); },
       [&](int first, int last) {
         const int nr = (last - first + 1) * rpt;
         for (int it = threadIdx.x; it < nr * M; it += kThreads) {
           const int q = it / M, t = it - q * M;
           const int row = (lo + first) * rpt + q;
-          st_dev(h1 + (size_t)t * d + row, h[(size_t)t * d + row] + part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t));
+          st_dev(h1 + (size_t)t * d + row, res[t * ncol + row - lo * rpt] + part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t));
         }
       });
 }
@@ -896,27 +1086,26 @@ template <typename WT, int MT>
 __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N,
                          XRegs<WT, MT>& xr) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const DevLayer& Ly = p.layers[l];
+  const auto& Ly = layer_tab(p)[l];
   const int d = p.d, F = p.F, E = p.E, M = p.M, S = p.S;
   const float* h1 = layer_h1(p, l);
   const float* br = Ly.b_router;
   const int has_bias = p.has_bias;
   float* logits = act_w(p, l, p.al.logits);
   float* a_s = act_w(p, l, p.al.a_s);
-  load_x<WT, MT>(xr, h1, d, reinterpret_cast<const WT*>(Ly.moe_norm), M, wave, lane, P.lrb);
-  row_rinv(sm, h1, M, d, p.eps);
+  load_x_norm<WT, MT>(xr, sm, h1, d, reinterpret_cast<const WT*>(Ly.moe_norm), M, d, p.eps, wave, lane, P.lrb);
   zero_part(sm);
+  if (has_bias) load_res(sm, br, nullptr, 0, 0, E, 1);
   __syncthreads();
-  constexpr int kRound = ((kPartBytes / 4) / (kWaves * 2 * MT)) & ~1;  // even: a pair stays in one round
+  const float* res = res_slice(sm);
+  constexpr int kRound = (kPartAcc / (kWaves * 2 * MT)) & ~1;  // even: a pair stays in one round
   const Misc* ms = sm.misc;
   const int rpt = P.rpt, lrb = P.lrb, n1 = P.n1, n = P.n, r_lo = P.lo, p_lo = P.lo2, fb_per = P.fb_per;
   run_gemv<WT, MT>(
-      sm, st, P, N, xr, [&](int, unsigned& tm, float (&tw)[MT], bool& ac) { all_tokens<MT>(M, tm, tw, ac); },
-      [=](int i) { return i < n1 ? i % kRound : (i - n1) % kRound; },
-      [=](int i) {
-        if (i == n - 1) return true;
-        if (i < n1) return i == n1 - 1 || ((i + 1) % kRound) == 0;
-        return ((i - n1 + 1) % kRound) == 0;
+      sm, st, P, N, xr,
+      [&](int i, Seg<MT>& sg) {
+        if (i < n1) seg_rounds<MT>(sg, i, 0, n1, kRound, M);
+        else seg_rounds<MT>(sg, i, n1, n, kRound, M);
       },
       [&](int first, int last) {
         if (first < n1) {
@@ -926,7 +1115,7 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
             const int e = (r_lo + first) * rpt + q;
             if (e >= E) continue;
             float v = part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t) * ms->rinv[t];
-            if (has_bias) v += br[e];
+            if (has_bias) v += res[e];
             st_dev(logits + (size_t)t * E + e, v);
           }
         } else {
@@ -943,6 +1132,13 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
           }
         }
       });
+}
+
+// slot of expert e in row t's top-k list, or -1
+__device__ __forceinline__ int slot_of(const Misc* ms, int t, int k, int e) {
+  for (int i = 0; i < k; ++i)
+    if (ms->ids[t * k + i] == e) return i;
+  return -1;
 }
 
 // Top-k over the router logits of every row (all CUs, redundantly), then the
@@ -1001,6 +1197,17 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
     if (lane == 0) ms->n_uni = __popcll(mm);
   }
   __syncthreads();
+  for (int u = threadIdx.x; u < ms->n_uni; u += kThreads) {
+    const int e = ms->uni[u];
+    unsigned m = 0;
+    for (int t = 0; t < M; ++t) {
+      const int sl = slot_of(ms, t, k, e);
+      ms->uslot[u * kMaxRows + t] = (signed char)sl;
+      if (sl >= 0) m |= 1u << t;
+    }
+    ms->umask[u] = m;
+  }
+  __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < M * k; i += kThreads) {
       if (p.t_ids) p.t_ids[(size_t)l * M * k + i] = ms->ids[i];
@@ -1009,19 +1216,6 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
     if (p.t_logits)
       for (int i = threadIdx.x; i < M * E; i += kThreads) p.t_logits[(size_t)l * M * E + i] = logits[i];
   }
-}
-
-// slot of expert e in row t's top-k list, or -1
-__device__ __forceinline__ int slot_of(const Misc* ms, int t, int k, int e) {
-  for (int i = 0; i < k; ++i)
-    if (ms->ids[t * k + i] == e) return i;
-  return -1;
-}
-__device__ __forceinline__ unsigned routed_mask(const Misc* ms, int M, int k, int e) {
-  unsigned m = 0;
-  for (int t = 0; t < M; ++t)
-    if (slot_of(ms, t, k, e) >= 0) m |= 1u << t;
-  return m;
 }
 
 // x registers for one tile from LDS rows: token t uses row rows[t] of [M][..][F]
@@ -1047,80 +1241,72 @@ __device__ __forceinline__ void load_x_lds(XRegs<WT, MT>& xr, const float* base,
 }
 
 // RG: shared-expert down projection y_s = sum_s Wd_s a_s (x from LDS), then
-// the routed gate/up rows for the union experts (x registers from RS):
-// a[t][slot][f] for rows routed to the expert.
+// the routed gate/up rows for the union experts (x = y from RS):
+// a[t][slot][f] for the rows routed to the expert.
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N,
-                         XRegs<WT, MT>& xr) {
+                                         const XRegs<WT, MT>& xr) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d = p.d, F = p.F, k = p.k, M = p.M, S = p.S;
-  const float* h1 = layer_h1(p, l);
   const float* as_g = act_f(p, l, p.al.a_s);
   float* a = act_w(p, l, p.al.a);
   float* ys = act_w(p, l, p.al.y_s);
-  row_rinv(sm, h1, M, d, p.eps);
-  // shared activations a_s [M][S][F] -> LDS
-  for (int i = threadIdx.x; i < M * S * F / 4; i += kThreads)
-    reinterpret_cast<float4*>(sm.xs)[i] = reinterpret_cast<const float4*>(as_g)[i];
+  // misc->rinv still holds RS's 1/rms of h1.  Shared activations a_s
+  // [M][S][F] -> LDS by DMA (whole KiB; F*4 bytes is a multiple of 1 KiB).
+  dma_to_lds((char*)sm.xs, (const char*)as_g, M * S * F * 4, wave, lane);
   zero_part(sm);
+  wait_all();
   __syncthreads();
   const Misc* ms = sm.misc;
-  XRegs<WT, MT> xsd;
-  constexpr int kRound = ((kPartBytes / 4) / (kWaves * 2 * MT)) & ~1;
-  const int n1 = P.n1, n = P.n, lrb = P.lrb, lrb2 = P.lrb2, rpt = P.rpt, rpt2 = P.rpt2, fb_per = P.fb_per;
-  const int sd_lo = P.lo, p_lo = P.lo2;
-  // shared-down units (S tiles, accumulated) use blocks 0.. of the first round
-  auto pre = [&](int i, unsigned& tm, float (&tw)[MT], bool& ac) {
+  constexpr int kRound = (kPartAcc / (kWaves * 2 * MT)) & ~1;  // even: a gate/up pair stays in one round
+  const int n1 = P.n1, n = P.n, nj = P.nj, lrb = P.lrb, lrb2 = P.lrb2, rpt = P.rpt, rpt2 = P.rpt2;
+  const int fb_per = P.fb_per, sd_lo = P.lo, p_lo = P.lo2;
+  XRegs<WT, MT> xw;  // a_s rows for the shared-down tiles, then y
+  run_gemv<WT, MT>(
+      sm, st, P, N, xw,
+      [&](int i, Seg<MT>& sg) {
+        seg_all<MT>(sg, M);
+        if (i < n1) {  // expert s of the shared down projection, all of this CU's j-blocks
+          const int sx = i / nj;
+          int ro[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) tw[t] = 1.f;
-    if (i < n1) {
-      const int sx = i % S;
-      tm = (1u << M) - 1u;
-      int ro[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) ro[t] = (t * S + sx) * F;
-      load_x_lds<WT, MT>(xsd, sm.xs, ro, tm, wave, lane, lrb);
-      ac = true;
-    } else {
-      const int pj = p_lo + ((i - n1) >> 1);
-      tm = routed_mask(ms, M, k, ms->uni[pj / fb_per]);
-      ac = false;
-    }
-  };
-  {
-    st.fill(sm, P, N, 0, wave, lane);
-    int round_first = 0;
-    for (int i = 0; i < n; ++i) {
-      unsigned tmask;
-      float tw[MT];
-      bool accum;
-      pre(i, tmask, tw, accum);
-      const int blk = i < n1 ? (i / S) : (i - n1) % kRound;
-      st.wait(i);
-      gemv_quarter<WT, MT>(st.slot(sm, i), i < n1 ? xsd : xr, tmask, tw,
-                           sm.part + (size_t)blk * (kWaves * 2 * MT) + wave * 2 * MT, accum, wave, lane);
-      st.fill(sm, P, N, i + 1, wave, lane);
-      const bool end = (i == n - 1) || (i == n1 - 1) || (i >= n1 && ((i - n1 + 1) % kRound) == 0);
-      if (end) {
-        __syncthreads();
-        if (round_first < n1) {
+          for (int t = 0; t < MT; ++t) ro[t] = (t * S + sx) * F;
+          load_x_lds<WT, MT>(xw, sm.xs, ro, sg.tmask, wave, lane, lrb);
+          sg.end = i + nj;
+          sg.blk0 = 0;
+          sg.accum = true;
+          sg.round_end = sg.end == n1;
+        } else {
+          if (i == n1) xw = xr;
+          const int k0 = i - n1;
+          int end = n1 + min(n - n1, (k0 / kRound + 1) * kRound);
+          if (M > 1) {  // one run per expert: its rows only
+            const int u = (p_lo + k0 / 2) / fb_per;
+            end = min(end, n1 + 2 * ((u + 1) * fb_per - p_lo));
+            sg.tmask = ms->umask[u];
+          }
+          sg.end = end;
+          sg.blk0 = k0 % kRound;
+          sg.accum = false;
+          sg.round_end = end == n || ((end - n1) % kRound) == 0;
+        }
+      },
+      [&](int first, int last) {
+        if (first < n1) {
           // shared-down j-blocks of this CU: y_s[t][j]
-          const int nunits = n1 / S;
-          for (int it = threadIdx.x; it < nunits * rpt * M; it += kThreads) {
+          for (int it = threadIdx.x; it < nj * rpt * M; it += kThreads) {
             const int u = it / (rpt * M), q = (it / M) % rpt, t = it % M;
             const int j = (sd_lo + u) * rpt + q;
             st_dev(ys + (size_t)t * d + j, part_row<MT>(sm.part, u, q, lrb, t));
           }
-          __syncthreads();
-          for (int z = threadIdx.x; z < kPartBytes / 4; z += kThreads) sm.part[z] = 0.f;
         } else {
-          const int k0 = round_first - n1;
-          const int npairs_r = (i - round_first + 1) / 2;
+          const int k0 = first - n1;
+          const int npairs_r = (last - first + 1) / 2;
           for (int it = threadIdx.x; it < npairs_r * rpt2 * M; it += kThreads) {
             const int pr = it / (rpt2 * M), q = (it / M) % rpt2, t = it % M;
             const int pj = p_lo + k0 / 2 + pr;
-            const int e = ms->uni[pj / fb_per], f = (pj % fb_per) * rpt2 + q;
-            const int sl = slot_of(ms, t, k, e);
+            const int u = pj / fb_per, f = (pj % fb_per) * rpt2 + q;
+            const int sl = ms->uslot[u * kMaxRows + t];
             if (sl < 0) continue;
             const float ri = ms->rinv[t];
             const float gv = part_row<MT>(sm.part, 2 * pr, q, lrb2, t) * ri;
@@ -1128,71 +1314,68 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
             st_dev(a + ((size_t)t * k + sl) * F + f, gv / (1.f + __expf(-gv)) * uv);
           }
         }
-        __syncthreads();
-        round_first = i + 1;
-      }
-    }
-  }
+      });
 }
 
-// DOWN: for this CU's blocks of output columns j, accumulate the union
-// experts (each row weighted by its routing weight), then
-// h2 = h1 + y_s + sum.  x rows a[t][slot] come from LDS when they fit.
+// DOWN: for this CU's j-blocks (output columns), accumulate the union
+// experts one after another (expert-major, so an expert's x rows are loaded
+// once), each row weighted by its routing weight; then h2 = h1 + y_s + sum.
+// The x rows a[t][slot] come from LDS when they fit.
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d = p.d, F = p.F, k = p.k, M = p.M;
-  const int U = P.U, rpt = P.rpt, lrb = P.lrb, lo = P.lo;
+  const int nj = P.nj, rpt = P.rpt, lrb = P.lrb, lo = P.lo, n = P.n;
   const float* h1 = layer_h1(p, l);
   const float* a_g = act_f(p, l, p.al.a);    // [M][k][F]
   const float* ys = act_f(p, l, p.al.y_s);   // [M][d]
   float* h2 = (l == p.L - 1) ? p.hidden_out : act_w(p, l, p.al.h2);
   const bool last_layer = (l == p.L - 1);
   const bool xl = (size_t)M * k * F * 4 <= (size_t)kXsBytes;
-  if (xl)
-    for (int i = threadIdx.x; i < M * k * F / 4; i += kThreads)
-      reinterpret_cast<float4*>(sm.xs)[i] = reinterpret_cast<const float4*>(a_g)[i];
+  if (xl) dma_to_lds((char*)sm.xs, (const char*)a_g, M * k * F * 4, wave, lane);
   zero_part(sm);
+  const bool has_shared = p.S > 0;
+  const int ncol = nj * rpt;
+  load_res(sm, h1, has_shared ? ys : nullptr, d, lo * rpt, ncol, M);
+  wait_all();
   __syncthreads();
   const Misc* ms = sm.misc;
-  const bool has_shared = p.S > 0;
+  const float* res = res_slice(sm);
   XRegs<WT, MT> xr;
   run_gemv<WT, MT>(
       sm, st, P, N, xr,
-      [&](int i, unsigned& tm, float (&tw)[MT], bool& ac) {
-        const int e = ms->uni[i % U];
-        tm = 0;
+      [&](int i, Seg<MT>& sg) {
+        const int u = i / nj;
+        unsigned tm = 0;
         int ro[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          tw[t] = 0.f;
+          sg.tw[t] = 0.f;
           ro[t] = 0;
           if (t < M) {
-            const int sl = slot_of(ms, t, k, e);
+            const int sl = ms->uslot[u * kMaxRows + t];
             if (sl >= 0) {
               ro[t] = (t * k + sl) * F;
-              tw[t] = ms->wts[t * k + sl];
+              sg.tw[t] = ms->wts[t * k + sl];
               tm |= 1u << t;
             }
           }
         }
-        if (xl) load_x_lds<WT, MT>(xr, sm.xs, ro, tm, wave, lane, lrb);
-        else load_x_lds<WT, MT>(xr, a_g, ro, tm, wave, lane, lrb);
-        ac = true;
+        load_x_lds<WT, MT>(xr, xl ? sm.xs : a_g, ro, tm, wave, lane, lrb);
+        sg.tmask = tm;
+        sg.end = i + nj;
+        sg.blk0 = 0;
+        sg.accum = true;
+        sg.round_end = sg.end == n;
       },
-      [](int) { return 0; }, [=](int i) { return ((i + 1) % U) == 0; },
-      [&](int first, int) {
-        const int jb = lo + first / U;
-        for (int it = threadIdx.x; it < rpt * M; it += kThreads) {
+      [&](int, int) {
+        for (int it = threadIdx.x; it < ncol * M; it += kThreads) {
           const int q = it / M, t = it - q * M;
-          const int j = jb * rpt + q;
-          float out = h1[(size_t)t * d + j] + part_row<MT>(sm.part, 0, q, lrb, t);
-          if (has_shared) out += ys[(size_t)t * d + j];
+          const int j = lo * rpt + q;
+          const float out = res[t * ncol + q] + part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t);
           if (last_layer) h2[(size_t)t * d + j] = out;
           else st_dev(h2 + (size_t)t * d + j, out);
         }
-        __syncthreads();
-        for (int i = threadIdx.x; i < kWaves * 2 * MT; i += kThreads) sm.part[i] = 0.f;
       });
 }
 
@@ -1242,20 +1425,19 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   const unsigned epoch0 = (unsigned)ms->epoch;
   __syncthreads();
   unsigned b = 0;
-  long long* stamp = p.stamps ? p.stamps + (size_t)blockIdx.x * 2 * (p.barriers + 1) : nullptr;
-  auto mark = [&](int slot) {
-    if (stamp && threadIdx.x == 0) stamp[slot] = wall_clock64();
-  };
-  // phase i starts at slot 2i (after barrier i) and ends at slot 2i+1
+  long long* stamp = p.stamps ? p.stamps + (size_t)blockIdx.x * 4 * (p.barriers + 1) : nullptr;
+  XRegs<WT, MT> xr_moe;
+  Stream st{0, 0, stamp, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}};
+  // phase i owns slots 4i..4i+3: start (after barrier i), tile loop start,
+  // tile loop end, end (before barrier i+1)
 #define MK_SYNC()                                   \
   do {                                              \
-    mark(2 * (int)b + 1);                           \
+    st.mark(3);                                     \
     if (!grid_sync(p, sm, epoch0 + ++b)) return;    \
-    mark(2 * (int)b);                               \
+    if (st.ts) st.ts += 4;                          \
+    st.mark(0);                                     \
   } while (0)
-  mark(0);
-  XRegs<WT, MT> xr_moe;
-  Stream st{0, 0};
+  st.mark(0);
   const Plan none{};
   Plan cur = p.attn ? plan_qkv<WT>(p, 0) : plan_rs<WT>(p, 0);
   for (int l = 0; l < p.L; ++l) {
@@ -1307,7 +1489,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   }
 #undef MK_SYNC
   wait_all();
-  mark(2 * (int)b + 1);
+  st.mark(3);
   if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u(p.sync + SyncLayout::kEpoch, epoch0 + b);
 }
 

@@ -82,6 +82,8 @@ int validate(const mk_config* c) {
   if (c->n_shared < 0 || c->n_shared > mk::kMaxShared) return fail(MK_ERR_UNSUPPORTED, "n_shared must be 0..4");
   if (!(c->rms_eps > 0.f)) return fail(MK_ERR_INVALID_ARG, "rms_eps must be > 0");
   if (c->rows < 1 || c->rows > 8) return fail(MK_ERR_UNSUPPORTED, "rows must be 1..8 in this build");
+  if ((size_t)c->rows * c->n_shared * c->d_ff * 4 > (size_t)mk::kXsBytes)
+    return fail(MK_ERR_UNSUPPORTED, "rows * n_shared * d_ff * 4 must fit %d bytes of LDS", mk::kXsBytes);
   if (c->rows_per_seq < 1 || c->rows % c->rows_per_seq) return fail(MK_ERR_INVALID_ARG, "rows_per_seq must divide rows");
   if (c->has_attn) {
     if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
@@ -162,6 +164,22 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
     int maxs = (c.kv_capacity + mk::kAttnTile - 1) / mk::kAttnTile;
     if (s > maxs) s = maxs;
     h->n_splits = s;
+  }
+  {
+    // epilogue residual slices (output columns of one CU, every row) live in
+    // 1024 floats of LDS
+    const int esz = c.dtype == MK_BF16 ? 2 : 4;
+    auto cols = [&](int row_elems) {
+      const int rpt = mk::kTileBytes / (row_elems * esz);
+      const int units = c.d_model / rpt;
+      return ((units + h->n_cu - 1) / h->n_cu) * rpt;
+    };
+    int ncol = cols(c.d_ff);
+    if (c.has_attn && cols(c.n_heads * c.head_dim) > ncol) ncol = cols(c.n_heads * c.head_dim);
+    if (ncol * M > 1024) {
+      delete h;
+      return fail(MK_ERR_UNSUPPORTED, "d_model * rows too large for %d CUs", prop.multiProcessorCount);
+    }
   }
   h->barriers = c.n_layers * (c.has_attn ? 6 : 3) - 1;
   // LDS: fixed carve-up (ring, x staging, per-row partial sums, misc)
