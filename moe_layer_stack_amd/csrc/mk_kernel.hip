@@ -834,6 +834,306 @@ __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stre
       });
 }
 
+// Online-softmax merge of one partial state (m_z, l_z, acc_z) into (M, L, a).
+__device__ __forceinline__ void softmax_merge(float& M, float& L, float4& a, float mz, float lz, float4 az) {
+  if (mz == -INFINITY) return;
+  const float Mn = fmaxf(M, mz);
+  const float c1 = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+  const float c2 = __expf(mz - Mn);
+  L = L * c1 + lz * c2;
+  a.x = a.x * c1 + az.x * c2; a.y = a.y * c1 + az.y * c2;
+  a.z = a.z * c1 + az.z * c2; a.w = a.w * c1 + az.w * c2;
+  M = Mn;
+}
+
+// The last split of (sequence, kv head g) to finish combines the S split
+// partials of each of its Q query vectors into o.  Partial record (kPartStride
+// floats): m, l, -, -, acc[hd] with acc = sum_t exp(s_t - m) v_t.  Thread =
+// (query, 4 dims, group of splits); each loads its splits' records in
+// batches of 8, merges them, and the split groups are merged through LDS
+// (cst, 6 floats per thread).
+__device__ __forceinline__ void attn_combine(const KParams& p, Smem sm, int l, int seq, int g, int Q, float* cst) {
+  const int S = p.n_splits, HG = p.H / p.G, rps = p.rps, hd = p.hd;
+  const float* pall = act_f(p, l, p.al.part) + ((size_t)((seq * p.G + g) * S) * Q) * kPartStride;
+  float* o = act_w(p, l, p.al.o);
+  const int QD = Q * (hd / 4);
+  const int ZG = QD >= kThreads ? 1 : kThreads / QD;
+  const int zper = (S + ZG - 1) / ZG;
+  for (int it = threadIdx.x; it < QD * ZG; it += kThreads) {
+    const int qd = it % QD, zg = it / QD;
+    const int q = qd / (hd / 4), d4 = qd % (hd / 4);
+    const int z0 = zg * zper, z1 = min(S, z0 + zper);
+    float M = -INFINITY, L = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int zb = z0; zb < z1; zb += 8) {
+      float2 ml[8];
+      float4 av[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (zb + u < z1) {
+          const float* rec = pall + ((size_t)(zb + u) * Q + q) * kPartStride;
+          ml[u] = *reinterpret_cast<const float2*>(rec);
+          av[u] = *reinterpret_cast<const float4*>(rec + 4 + 4 * d4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (zb + u < z1) softmax_merge(M, L, a, ml[u].x, ml[u].y, av[u]);
+    }
+    if (ZG == 1) {
+      const int row = seq * rps + q / HG, head = g * HG + q % HG;
+      float* dst = o + (size_t)row * (p.H * hd) + head * hd + 4 * d4;
+      const float inv = 1.f / L;
+      st_dev(dst, a.x * inv); st_dev(dst + 1, a.y * inv); st_dev(dst + 2, a.z * inv); st_dev(dst + 3, a.w * inv);
+    } else {
+      float* c = cst + (size_t)it * 6;
+      c[0] = M; c[1] = L; c[2] = a.x; c[3] = a.y; c[4] = a.z; c[5] = a.w;
+    }
+  }
+  if (ZG > 1) {
+    __syncthreads();
+    for (int qd = threadIdx.x; qd < QD; qd += kThreads) {
+      float M = -INFINITY, L = 0.f;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int zg = 0; zg < ZG; ++zg) {
+        const float* c = cst + (size_t)(zg * QD + qd) * 6;
+        softmax_merge(M, L, a, c[0], c[1], make_float4(c[2], c[3], c[4], c[5]));
+      }
+      const int q = qd / (hd / 4), d4 = qd % (hd / 4);
+      const int row = seq * rps + q / HG, head = g * HG + q % HG;
+      float* dst = o + (size_t)row * (p.H * hd) + head * hd + 4 * d4;
+      const float inv = 1.f / L;
+      st_dev(dst, a.x * inv); st_dev(dst + 1, a.y * inv); st_dev(dst + 2, a.z * inv); st_dev(dst + 3, a.w * inv);
+    }
+  }
+}
+
+// Queries of a task, their rotary embedding and this step's new k, v rows:
+// Qv[q][hd] (RoPE'd, scaled by 1/sqrt(hd)) and, for the rows whose position
+// falls in the split, the cache writes and the bf16-rounded copies newk,
+// newv [rps][hd] in LDS (the split's tiles may have been loaded before the
+// rows reached the cache).
+__device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, int l, int seq, int g, int Q,
+                                              int p_lo, int p_hi, const Plan& P, float* Qv, float* newk,
+                                              float* newv) {
+  const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
+  const int nrows_qkv = (p.H + 2 * p.G) * hd;
+  const float* qkv = act_f(p, l, p.al.qkv);
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int it = threadIdx.x; it < Q * (hd / 2); it += kThreads) {
+    const int q = it / (hd / 2), i = it % (hd / 2);
+    const int row = seq * rps + q / HG, head = g * HG + q % HG;
+    const float* src = qkv + (size_t)row * nrows_qkv + head * hd;
+    const float c = ms->rope[(row * 64 + i) * 2], sn = ms->rope[(row * 64 + i) * 2 + 1];
+    const float x0 = src[i], x1 = src[i + hd / 2];
+    Qv[q * hd + i] = (x0 * c - x1 * sn) * scale;
+    Qv[q * hd + i + hd / 2] = (x1 * c + x0 * sn) * scale;
+  }
+  uint16_t* kc = reinterpret_cast<uint16_t*>(const_cast<char*>(P.b0));
+  uint16_t* vc = reinterpret_cast<uint16_t*>(const_cast<char*>(P.b1));
+  for (int it = threadIdx.x; it < rps * (hd / 2); it += kThreads) {
+    const int rr = it / (hd / 2), i = it % (hd / 2);
+    const int row = seq * rps + rr;
+    const int pos = ms->pos[row];
+    if (pos < p_lo || pos >= p_hi) continue;
+    const float* ksrc = qkv + (size_t)row * nrows_qkv + p.H * hd + g * hd;
+    const float* vsrc = qkv + (size_t)row * nrows_qkv + (p.H + p.G) * hd + g * hd;
+    const float c = ms->rope[(row * 64 + i) * 2], sn = ms->rope[(row * 64 + i) * 2 + 1];
+    const float x0 = ksrc[i], x1 = ksrc[i + hd / 2];
+    const uint16_t k0 = f32_to_bf16(x0 * c - x1 * sn), k1 = f32_to_bf16(x1 * c + x0 * sn);
+    const uint16_t v0 = f32_to_bf16(vsrc[i]), v1 = f32_to_bf16(vsrc[i + hd / 2]);
+    kc[(size_t)pos * hd + i] = k0;
+    kc[(size_t)pos * hd + i + hd / 2] = k1;
+    vc[(size_t)pos * hd + i] = v0;
+    vc[(size_t)pos * hd + i + hd / 2] = v1;
+    newk[rr * 128 + i] = __uint_as_float((uint32_t)k0 << 16);
+    newk[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)k1 << 16);
+    newv[rr * 128 + i] = __uint_as_float((uint32_t)v0 << 16);
+    newv[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)v1 << 16);
+  }
+}
+
+// max over the four 16-lane rows (lanes with equal bits 0-3), in every lane
+__device__ __forceinline__ float max_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Split-KV GQA decode attention for tasks of at most NQ query vectors
+// (sequence rows * heads per kv head).  Task = (sequence, kv head, split) =
+// this CU.  The split streams as K, V tile pairs of 32 positions; wave w
+// takes positions 8w .. 8w+7 of every tile (its 2 KiB quarter, as in a GEMV
+// tile), a lane covering 8 dims (lane & 15) of one position per 1 KiB chunk,
+// for every query.  Each wave keeps an online-softmax state per query; the
+// four are merged through LDS into the split's partial.
+template <int NQ>
+__device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l, Stream& st, const Plan& P,
+                                               const Plan& N) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
+  const int Q = rps * HG;
+  const int S = p.n_splits;
+  const int ntask = p.n_seq * p.G * S;
+  Misc* ms = sm.misc;
+  float* Qv = sm.xs;                    // [NQ][128]
+  float* newk = Qv + NQ * 128;          // [rps][128]
+  float* newv = newk + kMaxRows * 128;  // [rps][128]
+  float* wst = newv + kMaxRows * 128;   // [kWaves][NQ][kPartStride] wave states; later combine scratch
+  const int task = blockIdx.x;
+  const bool active = task < ntask;
+  const int seq = active ? task / (p.G * S) : 0, g = active ? (task / S) % p.G : 0, s = active ? task % S : 0;
+  const int p_lo = P.a0, p_hi = P.a1;
+  if (active) attn_prologue(p, ms, l, seq, g, Q, p_lo, p_hi, P, Qv, newk, newv);
+  __syncthreads();
+  const int d0 = (lane & 15) * 8, prow = lane >> 4;
+  int newpos[kMaxRows];
+#pragma unroll
+  for (int rr = 0; rr < kMaxRows; ++rr) {
+    newpos[rr] = -1;
+    if (active && rr < rps) {
+      const int pos = ms->pos[seq * rps + rr];
+      if (pos >= p_lo && pos < p_hi) newpos[rr] = pos;
+    }
+  }
+  float qr[NQ][8], acc[NQ][8], m[NQ], lsum[NQ], pp[NQ][2];
+  int qlim[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[q][e] = 0.f;
+      qr[q][e] = (active && q < Q) ? Qv[q * 128 + d0 + e] : 0.f;
+    }
+    pp[q][0] = pp[q][1] = 0.f;
+    m[q] = -INFINITY;
+    lsum[q] = 0.f;
+    qlim[q] = (active && q < Q) ? min(p_hi - 1, ms->pos[seq * rps + q / HG]) : -1;  // last visible position
+  }
+  st.mark(1);
+  settle();
+  st.fill(sm, P, N, 0, wave, lane);
+  for (int i = 0; i < P.n; ++i) {
+    st.wait(i);
+    const char* sl = st.slot(sm, i) + wave * 2048 + lane * 16;
+    const uint4 raw0 = *reinterpret_cast<const uint4*>(sl);
+    const uint4 raw1 = *reinterpret_cast<const uint4*>(sl + 1024);
+    const int t0 = p_lo + (i >> 1) * kAttnTile;
+    const bool is_v = (i & 1) != 0;
+    float f[2][8];
+    unpack16<uint16_t>(raw0, f[0]);
+    unpack16<uint16_t>(raw1, f[1]);
+    int jpos[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      jpos[c] = t0 + wave * 8 + c * 4 + prow;
+#pragma unroll
+      for (int rr = 0; rr < kMaxRows; ++rr) {
+        if (newpos[rr] == jpos[c]) {
+          const float* src = (is_v ? newv : newk) + rr * 128 + d0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[c][e] = src[e];
+        }
+      }
+    }
+    if (!is_v) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        float sc[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            a0 = fmaf(f[c][e], qr[q][e], a0);
+            a1 = fmaf(f[c][e + 1], qr[q][e + 1], a1);
+          }
+          const float dsum = sum_row16(a0 + a1);
+          sc[c] = (jpos[c] <= qlim[q]) ? dsum : -INFINITY;
+        }
+        const float mt = max_rows(fmaxf(sc[0], sc[1]));
+        const float mn = fmaxf(m[q], mt);
+        const float corr = (mn == -INFINITY) ? 1.f : __expf(m[q] - mn);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pp[q][c] = (sc[c] == -INFINITY) ? 0.f : __expf(sc[c] - mn);
+        lsum[q] = lsum[q] * corr + pp[q][0] + pp[q][1];
+        m[q] = mn;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[q][e] *= corr;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(pp[q][0], f[0][e], fmaf(pp[q][1], f[1][e], acc[q][e]));
+    }
+    st.fill(sm, P, N, i + 1, wave, lane);
+  }
+  st.mark(2);
+  if (!active) return;
+  // wave states: lsum and acc summed over the wave's 4 position rows (each
+  // row's 16 lanes hold the same p, so one lane per row counts)
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const float lw = sum_rows(lsum[q]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[q][e] = sum_rows(acc[q][e]);
+    if (q < Q && lane < 16) {
+      float* dst = wst + (size_t)(wave * NQ + q) * kPartStride;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[4 + d0 + e] = acc[q][e];
+      if (lane == 0) {
+        dst[0] = m[q];
+        dst[1] = lw;
+      }
+    }
+  }
+  __syncthreads();
+  // merge the 4 wave states into the split partial
+  float* part = act_w(p, l, p.al.part) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
+  for (int it = threadIdx.x; it < Q * (hd / 4 + 1); it += kThreads) {
+    const int q = it / (hd / 4 + 1), k4 = it % (hd / 4 + 1);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wst[(size_t)(w * NQ + q) * kPartStride]);
+    float cw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = wst[(size_t)(w * NQ + q) * kPartStride];
+      cw[w] = (mw == -INFINITY) ? 0.f : __expf(mw - M);
+    }
+    float* dst = part + (size_t)q * kPartStride;
+    if (k4 == hd / 4) {
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) L += cw[w] * wst[(size_t)(w * NQ + q) * kPartStride + 1];
+      st_dev(dst + 0, M);
+      st_dev(dst + 1, L);
+    } else {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* src = wst + (size_t)(w * NQ + q) * kPartStride + 4 + 4 * k4;
+        a.x += cw[w] * src[0]; a.y += cw[w] * src[1]; a.z += cw[w] * src[2]; a.w += cw[w] * src[3];
+      }
+      st_dev(dst + 4 + 4 * k4, a.x); st_dev(dst + 5 + 4 * k4, a.y);
+      st_dev(dst + 6 + 4 * k4, a.z); st_dev(dst + 7 + 4 * k4, a.w);
+    }
+  }
+  wait_all();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = p.attn_cnt + ((size_t)l * p.n_seq + seq) * p.G + g;
+    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (old + 1u == (unsigned)S);
+    if (last) st_dev_u(cnt, 0u);
+    ms->last = last;
+  }
+  __syncthreads();
+  if (ms->last) attn_combine(p, sm, l, seq, g, Q, wst);
+}
+
 // Split-KV GQA attention.  Task = (sequence, kv head, split) = this CU.
 // Query vector q = rr*HG + hh is row seq*rps + rr, head g*HG + hh.  Every wave
 // reads every position of a tile; wave w owns the queries q = w, w+4, ...  A
@@ -1015,39 +1315,7 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
     ms->last = last;
   }
   __syncthreads();
-  if (ms->last) {
-    // combine the S partial softmax states of each query
-    const float* pall = act_f(p, l, p.al.part) + ((size_t)((seq * p.G + g) * S) * Q) * kPartStride;
-    for (int it = threadIdx.x; it < Q; it += kThreads) {
-      float mx = -INFINITY;
-      for (int z = 0; z < S; ++z) mx = fmaxf(mx, pall[((size_t)z * Q + it) * kPartStride]);
-      float L = 0.f;
-      for (int z = 0; z < S; ++z) {
-        const float* pz = pall + ((size_t)z * Q + it) * kPartStride;
-        const float e = pz[0] == -INFINITY ? 0.f : __expf(pz[0] - mx);
-        coef[it * S + z] = e;
-        L += pz[1] * e;
-      }
-      const float invL = 1.f / L;
-      for (int z = 0; z < S; ++z) coef[it * S + z] *= invL;
-    }
-    __syncthreads();
-    float* o = act_w(p, l, p.al.o);
-    for (int it = threadIdx.x; it < Q * (hd / 4); it += kThreads) {
-      const int q = it / (hd / 4), i4 = (it % (hd / 4)) * 4;
-      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-      for (int z = 0; z < S; ++z) {
-        const float cz = coef[q * S + z];
-        const float4 a = *reinterpret_cast<const float4*>(pall + ((size_t)z * Q + q) * kPartStride + 4 + i4);
-        num.x = fmaf(cz, a.x, num.x); num.y = fmaf(cz, a.y, num.y);
-        num.z = fmaf(cz, a.z, num.z); num.w = fmaf(cz, a.w, num.w);
-      }
-      const int row = seq * rps + q / HG, head = g * HG + q % HG;
-      float* dst = o + (size_t)row * (p.H * hd) + head * hd + i4;
-      st_dev(dst, num.x); st_dev(dst + 1, num.y); st_dev(dst + 2, num.z); st_dev(dst + 3, num.w);
-    }
-  }
+  if (ms->last) attn_combine(p, sm, l, seq, g, Q, coef);
 }
 
 // WO: h1 = h + Wo . o
@@ -1451,7 +1719,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
       }
       {
         const Plan nxt = plan_wo<WT>(p, l);
-        phase_attn<QW>(p, sm, l, st, cur, nxt);
+        if constexpr (QW == 1) phase_attn_dec<4>(p, sm, l, st, cur, nxt);
+        else phase_attn<QW>(p, sm, l, st, cur, nxt);
         MK_SYNC();
         st.advance(cur);
         cur = nxt;
@@ -1504,8 +1773,10 @@ extern "C" int mk_launch_kernel(const mk::KParams* pp, void* stream) {
   const int Q = p.attn ? p.q_per_task : 0;
   const void* fn;
   int idx;
-  // instantiations: weight dtype x token group (1 or 8) x queries per wave (1 or 8)
+  // instantiations: weight dtype x token group (1 or 8) x attention kind
+  // (1: decode attention, at most 4 query vectors per task; 8: up to 32)
   if (p.wide) {
+    if (Q > 4) return -2;
     fn = p.M == 1 ? (const void*)decode_step_kernel<float, 1, 1> : (const void*)decode_step_kernel<float, 8, 1>;
     idx = p.M == 1 ? 0 : 1;
   } else if (Q <= 4) {

@@ -91,6 +91,8 @@ int validate(const mk_config* c) {
     if (c->head_dim != 128) return fail(MK_ERR_UNSUPPORTED, "head_dim must be 128");
     if (c->rows_per_seq * (c->n_heads / c->n_kv_heads) > mk::kMaxQ)
       return fail(MK_ERR_UNSUPPORTED, "rows_per_seq * n_heads / n_kv_heads must be <= %d", mk::kMaxQ);
+    if (c->dtype == MK_F32 && c->rows_per_seq * (c->n_heads / c->n_kv_heads) > 4)
+      return fail(MK_ERR_UNSUPPORTED, "fp32 stacks support at most 4 query vectors per kv head and sequence");
     if (!is_row_size_ok((long long)c->n_heads * c->head_dim * es))
       return fail(MK_ERR_UNSUPPORTED, "n_heads*head_dim rows must be 1, 2, 4 or 8 KiB");
     if (c->d_model % (8192 / (c->n_heads * c->head_dim * es)))
