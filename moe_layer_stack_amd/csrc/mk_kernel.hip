@@ -77,11 +77,8 @@ __device__ __forceinline__ void unpack16<float>(uint4 v, float* w) {
   w[2] = __uint_as_float(v.z); w[3] = __uint_as_float(v.w);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
+// wave index as a wave-uniform (scalar) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // device-scope (write-through) stores for data other CUs read in this launch
 __device__ __forceinline__ void st_dev(float* p, float v) {
@@ -101,9 +98,11 @@ __device__ __forceinline__ void st_dev_u(unsigned* p, unsigned v) {
 // every later LDS access, which would serialise the ring.  Here the ring's
 // waits are all explicit (wait_tiles_ahead / wait_all), and every wait is a
 // compiler memory barrier so no LDS read of a slot moves above it.
-__device__ __forceinline__ void g2l(const void* g, void* lds_wave_base) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_wave_base);
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void g2l(const void* g, unsigned lds_wave_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "global_load_lds_dwordx4 %0, off nt"
@@ -128,6 +127,10 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
     MK_WAIT_ASM("s_waitcnt vmcnt(22)");
     return;
   }
+  if (ahead >= 8) {  // steady state of the grouped GEMV loop; conservative above 8
+    MK_WAIT_ASM("s_waitcnt vmcnt(16)");
+    return;
+  }
   switch (ahead) {
 #define MK_CASE(k, n)          \
   case k:                      \
@@ -147,7 +150,6 @@ __device__ __forceinline__ int ilog2(int x) { return 31 - __builtin_clz(x); }
 // ------------------------------------------------------------------ LDS carve-up
 
 struct Misc {
-  KParams p;  // kernel arguments, read from LDS (keeps them off the vector-memory counter)
   int pos[kMaxRows];
   int ids[kMaxRows * kMaxTopK];
   float wts[kMaxRows * kMaxTopK];
@@ -162,6 +164,7 @@ struct Misc {
   signed char uslot[kMaxExperts * kMaxRows];   // [u][t]: top-k slot of expert u in row t, or -1
   unsigned char used[kMaxExperts];
   float rope[kMaxRows * 64 * 2];  // (cos, sin) per row and frequency (head_dim 128)
+  float zs[kMaxRows * kMaxExperts];  // router logits of the step's rows
 };
 static_assert(sizeof(Misc) <= kMiscBytes, "misc region too small");
 
@@ -484,7 +487,7 @@ __device__ __forceinline__ Win build_win(const Plan& P, int w0, const Misc* ms, 
 }
 
 // issue this wave's quarter of tile j (of the window's plan) into `slot`
-__device__ __forceinline__ void issue_tile(const Win& w, int j, char* slot, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(const Win& w, int j, unsigned slot_lds, int wave, int lane) {
   const int idx = j - w.w0;
   const unsigned lo = __builtin_amdgcn_readlane(w.lo, idx);
   const unsigned hi = __builtin_amdgcn_readlane(w.hi, idx);
@@ -492,14 +495,15 @@ __device__ __forceinline__ void issue_tile(const Win& w, int j, char* slot, int 
   const int valid = kTileBytes - (int)((hi >> 27) << 8);
   const int off0 = wave * 2048 + lane * 16;
   const int off1 = off0 + 1024;
-  g2l(g + (off0 < valid ? off0 : 0), slot + wave * 2048);
-  g2l(g + (off1 < valid ? off1 : 0), slot + wave * 2048 + 1024);
+  g2l(g + (off0 < valid ? off0 : 0), slot_lds + wave * 2048);
+  g2l(g + (off1 < valid ? off1 : 0), slot_lds + wave * 2048 + 1024);
 }
 
 // Copy `bytes` (a multiple of 1 KiB) from global memory to LDS by DMA, 1 KiB
 // per wave instruction.  Completion needs wait_all() and a workgroup sync.
 __device__ __forceinline__ void dma_to_lds(char* lds, const char* g, int bytes, int wave, int lane) {
-  for (int c = wave * 1024; c < bytes; c += kWaves * 1024) g2l(g + c + lane * 16, lds + c);
+  const unsigned base = lds_addr(lds);
+  for (int c = wave * 1024; c < bytes; c += kWaves * 1024) g2l(g + c + lane * 16, base + c);
 }
 
 // The stream of one phase followed by the next: tile j < cur.n is the
@@ -511,6 +515,8 @@ struct Stream {
   int issued;
   long long* ts;  // this phase's 4 timestamp slots, or null
   Win wc, wn;     // address windows of the current and the next plan
+  int islot;      // ring slot of tile `issued`
+  unsigned ring_lds;
   __device__ __forceinline__ void mark(int k) const {
     if (ts && threadIdx.x == 0) ts[k] = wall_clock64();
   }
@@ -520,11 +526,12 @@ struct Stream {
   // issue while ring slots are free; `consumed` tiles of cur are done
   __device__ __forceinline__ void fill(Smem sm, const Plan& cur, const Plan& nxt, int consumed, int wave,
                                        int lane) {
+    // The slots being refilled held tiles whose reads this wave has already
+    // consumed (their values fed the arithmetic), so no LDS wait is needed.
     const int limit = min(consumed + kRing, cur.n + nxt.n);
-    if (issued >= limit) return;
-    wait_lgkm0();  // this wave's reads of the slots being refilled are done
     for (; issued < limit; ++issued) {
-      char* s = slot(sm, issued);
+      const unsigned s = ring_lds + (unsigned)islot * kTileBytes;
+      islot = islot == kRing - 1 ? 0 : islot + 1;
       if (issued < cur.n) {
         if ((unsigned)(issued - wc.w0) >= 64u) wc = build_win(cur, issued, sm.misc, lane);
         issue_tile(wc, issued, s, wave, lane);
@@ -665,10 +672,12 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
   constexpr int EPL = XRegs<WT, MT>::EPL;
   constexpr int NV = G * 2 * MT;
   uint4 wv[G][2];
+  const int rs0 = (st.slot0 + i) % kRing;
 #pragma unroll
   for (int u = 0; u < G; ++u) {
     if (u < g) {
-      const char* sl = st.slot(sm, i + u) + wave * 2048 + lane * 16;
+      const int rs = rs0 + u < kRing ? rs0 + u : rs0 + u - kRing;
+      const char* sl = sm.ring + (size_t)rs * kTileBytes + wave * 2048 + lane * 16;
       wv[u][0] = *reinterpret_cast<const uint4*>(sl);
       wv[u][1] = *reinterpret_cast<const uint4*>(sl + 1024);
     }
@@ -747,7 +756,7 @@ template <typename WT, int MT, class SegFn, class EpiFn>
 __device__ __forceinline__ void run_gemv(Smem sm, Stream& st, const Plan& cur, const Plan& nxt, XRegs<WT, MT>& xr,
                                          SegFn seg, EpiFn epi) {
   constexpr int G = GroupOf<MT>::G;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   st.mark(1);
   settle();
   st.fill(sm, cur, nxt, 0, wave, lane);
@@ -809,7 +818,7 @@ __device__ __forceinline__ void seg_rounds(Seg<MT>& sg, int i, int base, int end
 // QKV: raw projections of (h * g1); the row scale rinv is applied in the epilogue.
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int d = p.d, M = p.M;
   const int nrows = P.a0 + 2 * P.a1;
   const float* h = layer_in(p, l);
@@ -971,7 +980,7 @@ __device__ __forceinline__ float max_rows(float v) {
 template <int NQ>
 __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l, Stream& st, const Plan& P,
                                                const Plan& N) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
   const int Q = rps * HG;
   const int S = p.n_splits;
@@ -1142,7 +1151,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
 // cache, so the positions written by this step are taken from LDS.
 template <int QW>
 __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
   const int Q = rps * HG;
   const int S = p.n_splits;
@@ -1321,7 +1330,7 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
 // WO: h1 = h + Wo . o
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_wo(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int M = p.M, d = p.d;
   const int K = p.H * p.hd;
   const float* o = act_f(p, l, p.al.o);
@@ -1353,7 +1362,7 @@ __device__ __forceinline__ void phase_wo(const KParams& p, Smem sm, int l, Strea
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N,
                          XRegs<WT, MT>& xr) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const auto& Ly = layer_tab(p)[l];
   const int d = p.d, F = p.F, E = p.E, M = p.M, S = p.S;
   const float* h1 = layer_h1(p, l);
@@ -1414,47 +1423,37 @@ __device__ __forceinline__ int slot_of(const Misc* ms, int t, int k, int e) {
 // logits ranked by lower expert id; weights are softmax probabilities
 // renormalised over the chosen set.
 __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int E = p.E, k = p.k, M = p.M;
   const float* logits = act_f(p, l, p.al.logits);
   Misc* ms = sm.misc;
   for (int e = threadIdx.x; e < kMaxExperts; e += kThreads) ms->used[e] = 0;
+  for (int it = threadIdx.x; it < M * kMaxExperts; it += kThreads) {
+    const int t = it / kMaxExperts, e = it % kMaxExperts;
+    ms->zs[it] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+  }
   __syncthreads();
   for (int t = wave; t < M; t += kWaves) {
-    const float z = lane < E ? logits[(size_t)t * E + lane] : -INFINITY;
-    bool taken = lane >= E;
-    const float zmax = wave_max(z);
-    const float pz = lane < E ? __expf(z - zmax) : 0.f;
-    float psum = 0.f;
-    int sel[kMaxTopK];
+    // lane e: rank of expert e among the row's logits (larger first, equal
+    // logits by lower id), from broadcast reads of the staged row
+    const float* zr = ms->zs + t * kMaxExperts;
+    const float z = zr[lane];
+    int rank = 0;
+    float zmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kMaxTopK; ++i) {
-      sel[i] = 0;
-      if (i < k) {
-        float bz = taken ? -INFINITY : z;
-        int bi = taken ? 1 << 30 : lane;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float oz = __shfl_xor(bz, o);
-          const int oi = __shfl_xor(bi, o);
-          if (oz > bz || (oz == bz && oi < bi)) { bz = oz; bi = oi; }
-        }
-        if (lane == bi) taken = true;
-        sel[i] = bi;
-        psum += __shfl(pz, bi);
-      }
+    for (int j = 0; j < kMaxExperts; j += 4) {
+      const float4 o = *reinterpret_cast<const float4*>(zr + j);
+      rank += (o.x > z || (o.x == z && j < lane)) + (o.y > z || (o.y == z && j + 1 < lane)) +
+              (o.z > z || (o.z == z && j + 2 < lane)) + (o.w > z || (o.w == z && j + 3 < lane));
+      zmax = fmaxf(zmax, fmaxf(fmaxf(o.x, o.y), fmaxf(o.z, o.w)));
     }
-#pragma unroll
-    for (int i = 0; i < kMaxTopK; ++i) {
-      if (i < k) {
-        const int e = sel[i];
-        const float pe = __shfl(pz, e);
-        if (lane == 0) {
-          ms->ids[t * k + i] = e;
-          ms->wts[t * k + i] = pe / psum;
-          ms->used[e] = 1;
-        }
-      }
+    const bool sel = lane < E && rank < k;
+    const float pz = sel ? __expf(z - zmax) : 0.f;
+    const float psum = sum_rows(sum_row16(pz));
+    if (sel) {
+      ms->ids[t * k + rank] = lane;
+      ms->wts[t * k + rank] = pz / psum;
+      ms->used[lane] = 1;
     }
   }
   __syncthreads();
@@ -1514,7 +1513,7 @@ __device__ __forceinline__ void load_x_lds(XRegs<WT, MT>& xr, const float* base,
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N,
                                          const XRegs<WT, MT>& xr) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int d = p.d, F = p.F, k = p.k, M = p.M, S = p.S;
   const float* as_g = act_f(p, l, p.al.a_s);
   float* a = act_w(p, l, p.al.a);
@@ -1591,7 +1590,7 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
 // The x rows a[t][slot] come from LDS when they fit.
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int d = p.d, F = p.F, k = p.k, M = p.M;
   const int nj = P.nj, rpt = P.rpt, lrb = P.lrb, lo = P.lo, n = P.n;
   const float* h1 = layer_h1(p, l);
@@ -1695,7 +1694,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   unsigned b = 0;
   long long* stamp = p.stamps ? p.stamps + (size_t)blockIdx.x * 4 * (p.barriers + 1) : nullptr;
   XRegs<WT, MT> xr_moe;
-  Stream st{0, 0, stamp, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}};
+  Stream st{0, 0, stamp, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring)};
   // phase i owns slots 4i..4i+3: start (after barrier i), tile loop start,
   // tile loop end, end (before barrier i+1)
 #define MK_SYNC()                                   \
