@@ -31,7 +31,9 @@
  *   s_gate, s_up [n_shared][F][d];  s_down [n_shared][d][F]
  * bf16 means the upper 16 bits of an IEEE binary32 (round-to-nearest-even
  * from fp32 wherever the library rounds).  Hidden rows are fp32 [M][d].
- * KV cache (bf16): k and v each [L][n_seq][G][capacity][hd], contiguous.
+ * KV cache (bf16): k and v each [L][kv->n_seq][G][capacity][hd], contiguous;
+ * a step uses sequences 0 .. rows/rows_per_seq - 1 of it (a cache may hold
+ * more sequences than one handle's step, e.g. batch 1 over a batch-8 cache).
  * Row r belongs to sequence r / rows_per_seq and sits at positions[r]; a
  * step writes the row's k, v (RoPE applied to k, rounded to bf16) at that
  * position and attends to cache positions 0..positions[r] of its sequence.

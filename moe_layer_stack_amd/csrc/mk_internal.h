@@ -75,6 +75,7 @@ struct KParams {
   // shapes
   int L, d, E, k, S, F;
   int H, G, hd, M, rps, n_seq, cap;
+  int kv_seqs;               // sequences in the caller's cache (its layer stride); >= n_seq
   int attn, has_bias, wide;  // wide: weights are fp32
   float eps, theta;
   int n_splits;              // KV splits per (seq, kv head)

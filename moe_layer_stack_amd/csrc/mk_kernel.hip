@@ -363,7 +363,7 @@ __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int 
   P.a0 = s * sl;
   P.a1 = min(P.a0 + sl, npos);
   P.n = P.a1 > P.a0 ? 2 * ((P.a1 - P.a0 + kAttnTile - 1) / kAttnTile) : 0;
-  const size_t kv_base = ((((size_t)l * p.n_seq + seq) * p.G + g) * (size_t)p.cap) * p.hd;
+  const size_t kv_base = ((((size_t)l * p.kv_seqs + seq) * p.G + g) * (size_t)p.cap) * p.hd;
   P.b0 = reinterpret_cast<const char*>(p.kcache + kv_base);
   P.b1 = reinterpret_cast<const char*>(p.vcache + kv_base);
   P.lo = task;

@@ -304,6 +304,7 @@ int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* position
   p.H = c.has_attn ? c.n_heads : 0; p.G = c.has_attn ? c.n_kv_heads : 1; p.hd = c.has_attn ? c.head_dim : 0;
   p.M = c.rows; p.rps = c.rows_per_seq; p.n_seq = n_seq;
   p.cap = c.has_attn ? kv->capacity : 0;
+  p.kv_seqs = c.has_attn ? kv->n_seq : 0;
   p.has_bias = c.has_router_bias ? 1 : 0;
   p.wide = c.dtype == MK_F32 ? 1 : 0;
   p.eps = c.rms_eps; p.theta = c.rope_theta;

@@ -1,0 +1,270 @@
+"""GPU checks through the C ABI that do not need the oracle's arithmetic, or
+only a little of it: exact identities of the method, determinism, device-side
+error reporting, the batch and verify equivalences, multi-step feedback and a
+full-depth run of the 92-layer stack."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_layer_stack_amd as mk
+    mk.lib()
+    return torch
+
+
+def _stack(w, n_layers=None):
+    from synth.stack import DeviceStack
+    return DeviceStack(w, n_layers=n_layers)
+
+
+def test_zero_router_routes_first_k_with_equal_weights(env):
+    """W_r = 0 and b = 0: every logit is exactly 0, so the first k experts are
+    chosen (equal values rank the lower id first) with weights exactly 1/k."""
+    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+    from synth.workloads import MOE16_B8
+    torch = env
+    w = MOE16_B8
+    _say(f"zero router {w.name} L=2")
+    st = _stack(w, 2)
+    for t in st.layers:
+        t["wr"].zero_()
+        t["br"].zero_()
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        out = run.step(hid, w.positions(0))
+        ids, wts, logits = run.trace()
+        assert (logits == 0).all()
+        assert (ids == np.arange(w.k, dtype=np.int32)).all(), ids[:, 0]
+        assert (wts == np.float32(1.0) / np.float32(w.k)).all(), np.unique(wts)
+        ref, rep = oracle_walk(st, hid.cpu().numpy(), w.positions(0), ids)
+        assert not rep["mismatch"]
+        assert_close(out.cpu().numpy(), ref, tolerances(w), "zero router")
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_zero_gates_leave_the_residual_exactly(env, M):
+    """Every gate projection zero: silu(0) = 0, so every expert returns 0 and
+    the step maps hidden_in to itself bit for bit."""
+    from parity_util import GpuRun
+    from synth.workloads import MOE16_B8
+    torch = env
+    w = MOE16_B8.with_(M=M)
+    _say(f"zero gates {w.name} M={M} L=3")
+    st = _stack(w, 3)
+    for t in st.layers:
+        t["wg"].zero_()
+        t["sg"].zero_()
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        out = run.step(hid, w.positions(0))
+        assert torch.equal(out, hid), (out - hid).abs().max().item()
+    finally:
+        run.close()
+
+
+def test_identical_experts_make_routing_irrelevant(env):
+    """All routed experts equal to expert 0: the weights sum to 1, so the
+    output equals h + y_0 + shared whatever the router picks.  Two routers
+    (the generated one and its negation) must give the same result."""
+    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+    from synth.workloads import MOE16_B8
+    torch = env
+    w = MOE16_B8
+    _say(f"identical experts {w.name} L=2")
+    st = _stack(w, 2)
+    for t in st.layers:
+        for k in ("wg", "wu", "wd"):
+            t[k][1:].copy_(t[k][0:1].expand_as(t[k][1:]))
+    hid = st.hidden(0)
+    run = GpuRun(st)
+    try:
+        out_a = run.step(hid, w.positions(0)).clone()
+        ids_a, _, _ = run.trace()
+        for t in st.layers:
+            t["wr"].neg_()
+            t["br"].neg_()
+        out_b = run.step(hid, w.positions(0)).clone()
+        ids_b, _, _ = run.trace()
+        assert (np.sort(ids_a, axis=-1) != np.sort(ids_b, axis=-1)).any(), "negated router chose the same experts"
+        assert_close(out_b.cpu().numpy(), out_a.cpu().numpy(), tolerances(w), "identical experts, two routers")
+        ref, rep = oracle_walk(st, hid.cpu().numpy(), w.positions(0), ids_b)
+        assert_close(out_b.cpu().numpy(), ref, tolerances(w), "identical experts vs oracle")
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("name", ["moe16_b8", "attn92_b8"])
+def test_repeated_steps_are_bitwise_identical(env, name):
+    """No floating-point atomics on the path: the same inputs give the same
+    bits (the attention step rewrites the same KV rows with the same values)."""
+    from parity_util import GpuRun
+    from synth import workloads
+    torch = env
+    w = {"moe16_b8": workloads.MOE16_B8, "attn92_b8": workloads.ATTN92_B8}[name]
+    _say(f"determinism {name} L=2")
+    st = _stack(w, 2)
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        a = run.step(hid, w.positions(0)).clone()
+        ta = [x.copy() for x in run.trace()]
+        b = run.step(hid, w.positions(0)).clone()
+        tb = run.trace()
+        assert torch.equal(a, b)
+        for x, y in zip(ta, tb):
+            assert np.array_equal(x, y)
+    finally:
+        run.close()
+
+
+def test_bad_positions_are_reported_and_the_handle_recovers(env):
+    """A position outside [0, capacity) or two rows of one sequence at the same
+    position: the step writes nothing it should not and the next mk_sync
+    returns MK_ERR_INVALID_ARG; the following valid step is unaffected."""
+    import moe_layer_stack_amd as mk
+    from parity_util import GpuRun
+    from synth.workloads import VERIFY92_M8
+    torch = env
+    w = VERIFY92_M8
+    _say(f"bad positions {w.name} L=2")
+    st = _stack(w, 2)
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        good = run.step(hid, w.positions(0)).clone()
+        kv0 = [(st.kc[l].clone(), st.vc[l].clone()) for l in range(st.L)]
+        for bad in ([w.capacity] + w.positions(0)[1:], [w.past] * w.M, [-1] + w.positions(0)[1:]):
+            _say(f"bad positions {bad}")
+            pos = torch.as_tensor(np.asarray(bad, dtype=np.int32), device="cuda")
+            out = torch.full_like(hid, 7.0)
+            mk.mk_decode_step(run.h, hid.data_ptr(), pos.data_ptr(), st.kv(), out.data_ptr(), 0)
+            assert mk.mk_sync(run.h, 0) == mk.MK_ERR_INVALID_ARG
+            assert (out == 7.0).all(), "a rejected step wrote its output"
+            for l in range(st.L):
+                assert torch.equal(st.kc[l], kv0[l][0]) and torch.equal(st.vc[l], kv0[l][1]), "KV written"
+        again = run.step(hid, w.positions(0))
+        assert torch.equal(again, good)
+    finally:
+        run.close()
+
+
+def test_batch8_row_equals_batch1(env):
+    """Sequences are independent: row 0 of a batch-8 step equals the batch-1
+    step of sequence 0 (same row, same position, same cache)."""
+    from parity_util import GpuRun, assert_close, tolerances
+    from synth.workloads import ATTN92_B8
+    torch = env
+    w8 = ATTN92_B8
+    _say(f"batch 8 row 0 vs batch 1 {w8.name} L=3")
+    st = _stack(w8, 3)
+    hid = st.hidden(0)
+    r8 = GpuRun(st)
+    r1 = GpuRun(st, rows=1, rows_per_seq=1)
+    try:
+        o8 = r8.step(hid, w8.positions(0)).clone()
+        o1 = r1.step(hid[:1].contiguous(), w8.positions(0)[:1]).clone()
+        assert_close(o1.cpu().numpy(), o8[:1].cpu().numpy(), tolerances(w8), "batch-8 row 0 vs batch 1")
+        assert (r1.trace()[0][:, 0] == r8.trace()[0][:, 0]).all()
+    finally:
+        r8.close()
+        r1.close()
+
+
+def test_verify_rows_equal_sequential_decode(env):
+    """Verify row r (positions p..p+7 of one sequence, causal among the
+    drafts) equals decode step r run on its own after steps 0..r-1."""
+    from parity_util import GpuRun, assert_close, tolerances
+    from synth.workloads import VERIFY92_M8
+    torch = env
+    w = VERIFY92_M8
+    _say(f"verify vs sequential decode {w.name} L=2")
+    st = _stack(w, 2)
+    kv0 = [(st.kc[l].clone(), st.vc[l].clone()) for l in range(st.L)]
+    hid = st.hidden(0)
+    pos = w.positions(0)
+    rv = GpuRun(st)
+    try:
+        ov = rv.step(hid, pos).clone()
+    finally:
+        rv.close()
+    for l in range(st.L):
+        st.kc[l].copy_(kv0[l][0])
+        st.vc[l].copy_(kv0[l][1])
+    r1 = GpuRun(st, rows=1, rows_per_seq=1)
+    try:
+        for r in range(w.M):
+            o1 = r1.step(hid[r:r + 1].contiguous(), [pos[r]])
+            assert_close(o1.cpu().numpy(), ov[r:r + 1].cpu().numpy(), tolerances(w), f"verify row {r}")
+    finally:
+        r1.close()
+
+
+def test_moe16_feedback_steps(env):
+    """Four steps of the 16-layer stack with the output fed back; every step
+    matches the oracle run on the GPU's input of that step."""
+    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+    from synth.workloads import MOE16_B1
+    torch = env
+    w = MOE16_B1
+    _say(f"feedback {w.name} 4 steps")
+    st = _stack(w)
+    run = GpuRun(st)
+    try:
+        h = st.hidden(0)
+        for s in range(4):
+            out = run.step(h, w.positions(s))
+            ids, _, _ = run.trace()
+            ref, rep = oracle_walk(st, h.cpu().numpy(), w.positions(s), ids)
+            assert not rep["mismatch"], rep["mismatch"][:3]
+            c = assert_close(out.cpu().numpy(), ref, tolerances(w), f"step {s}")
+            _say(f"step {s} {c} forced={rep['forced']}")
+            h = out.clone()
+    finally:
+        run.close()
+
+
+@pytest.mark.timeout(900)
+def test_attn92_full_depth_batch1_and_batch8_row(env):
+    """The benchmark's stack at full depth (92 layers): batch 1 against the
+    oracle, and row 0 of the batch-8 launch against batch 1."""
+    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+    from synth.workloads import ATTN92_B8
+    torch = env
+    w8 = ATTN92_B8
+    _say(f"full depth {w8.name} L={w8.L}")
+    st = _stack(w8)
+    kv0 = [tuple(x[:1].copy() for x in st.host_kv(l)) for l in range(st.L)]  # sequence 0
+    hid = st.hidden(0)
+    pos = w8.positions(0)
+    r1 = GpuRun(st, rows=1, rows_per_seq=1)
+    try:
+        o1 = r1.step(hid[:1].contiguous(), pos[:1]).clone()
+        ids1, _, _ = r1.trace()
+    finally:
+        r1.close()
+    _say("full depth: oracle walk (92 layers)")
+    ref, rep = oracle_walk(st, hid[:1].cpu().numpy(), pos[:1], ids1, kv_hosts=kv0)
+    assert not rep["mismatch"], rep["mismatch"][:3]
+    c = assert_close(o1.cpu().numpy(), ref, tolerances(w8), "full depth batch 1")
+    _say(f"full depth batch 1 {c} forced={rep['forced']}")
+    r8 = GpuRun(st)
+    try:
+        o8 = r8.step(hid, pos).clone()
+    finally:
+        r8.close()
+    assert_close(o8[:1].cpu().numpy(), o1.cpu().numpy(), tolerances(w8), "full depth batch-8 row 0")
+    assert bool(torch.isfinite(o8).all())
