@@ -96,7 +96,10 @@ typedef struct mk_config {
   int32_t n_kv_heads;      /* G, H % G == 0, H / G <= 8 */
   int32_t head_dim;        /* hd = 128 */
   float rope_theta;        /* > 0 */
-  int32_t rows;            /* M, 1..64, fixed per handle */
+  int32_t rows;            /* M, 1..64, fixed per handle.  Above 8, a multiple of 8 with
+                              rows_per_seq dividing 8: such a step runs as rows/8
+                              launches of 8 rows (whole sequences) on the stream,
+                              each streaming every layer's weights */
   int32_t rows_per_seq;    /* 1 for decode; > 1 for a verify pass; divides M */
   int32_t kv_capacity;     /* positions per sequence in the cache (attention stacks) */
 } mk_config;
@@ -129,7 +132,8 @@ typedef struct mk_info {
   int32_t n_cu;              /* workgroups in the persistent grid (one per CU) */
   int32_t threads;           /* threads per workgroup */
   int32_t lds_bytes;         /* dynamic LDS per workgroup */
-  int32_t barriers_per_step; /* grid barriers one step executes */
+  int32_t barriers_per_step; /* grid barriers one launch executes (a step of more than 8
+                                rows is rows/8 launches) */
   int32_t attn_splits;       /* KV splits per (sequence, kv head) */
   int64_t workspace_bytes;   /* device memory owned by the handle */
 } mk_info;
@@ -168,7 +172,8 @@ int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits);
  * i, into slots 4i .. 4i+3: the phase start (after the preceding grid
  * barrier), the start and the end of its weight-tile loop, and the phase end
  * (before the next barrier).  Phases in order per layer: QKV, ATTN, WO
- * (attention stacks), RS, RG, DOWN. */
+ * (attention stacks), RS, RG, DOWN.  A step of more than 8 rows leaves the
+ * stamps of its last launch. */
 int mk_set_timing(mk_handle* h, int64_t* stamps);
 
 /* Launch geometry and workspace size of a handle. */

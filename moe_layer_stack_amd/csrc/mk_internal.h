@@ -76,6 +76,7 @@ struct KParams {
   int L, d, E, k, S, F;
   int H, G, hd, M, rps, n_seq, cap;
   int kv_seqs;               // sequences in the caller's cache (its layer stride); >= n_seq
+  int row0, seq0, Mt;        // this launch's first row and sequence within the step; rows of the step
   int attn, has_bias, wide;  // wide: weights are fp32
   float eps, theta;
   int n_splits;              // KV splits per (seq, kv head)

@@ -363,7 +363,7 @@ __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int 
   P.a0 = s * sl;
   P.a1 = min(P.a0 + sl, npos);
   P.n = P.a1 > P.a0 ? 2 * ((P.a1 - P.a0 + kAttnTile - 1) / kAttnTile) : 0;
-  const size_t kv_base = ((((size_t)l * p.kv_seqs + seq) * p.G + g) * (size_t)p.cap) * p.hd;
+  const size_t kv_base = ((((size_t)l * p.kv_seqs + p.seq0 + seq) * p.G + g) * (size_t)p.cap) * p.hd;
   P.b0 = reinterpret_cast<const char*>(p.kcache + kv_base);
   P.b1 = reinterpret_cast<const char*>(p.vcache + kv_base);
   P.lo = task;
@@ -1477,11 +1477,11 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < M * k; i += kThreads) {
-      if (p.t_ids) p.t_ids[(size_t)l * M * k + i] = ms->ids[i];
-      if (p.t_w) p.t_w[(size_t)l * M * k + i] = ms->wts[i];
+      if (p.t_ids) p.t_ids[((size_t)l * p.Mt + p.row0) * k + i] = ms->ids[i];
+      if (p.t_w) p.t_w[((size_t)l * p.Mt + p.row0) * k + i] = ms->wts[i];
     }
     if (p.t_logits)
-      for (int i = threadIdx.x; i < M * E; i += kThreads) p.t_logits[(size_t)l * M * E + i] = logits[i];
+      for (int i = threadIdx.x; i < M * E; i += kThreads) p.t_logits[((size_t)l * p.Mt + p.row0) * E + i] = logits[i];
   }
 }
 

@@ -38,6 +38,10 @@ bool is_row_size_ok(long long bytes) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// rows of one launch: a step of more than kMaxRows rows runs as
+// rows / kMaxRows launches of whole sequences
+int launch_rows(const mk_config& c) { return c.rows < mk::kMaxRows ? c.rows : mk::kMaxRows; }
+
 }  // namespace
 
 struct mk_handle {
@@ -81,8 +85,11 @@ int validate(const mk_config* c) {
     return fail(MK_ERR_UNSUPPORTED, "top_k must be 1..min(n_experts, 8)");
   if (c->n_shared < 0 || c->n_shared > mk::kMaxShared) return fail(MK_ERR_UNSUPPORTED, "n_shared must be 0..4");
   if (!(c->rms_eps > 0.f)) return fail(MK_ERR_INVALID_ARG, "rms_eps must be > 0");
-  if (c->rows < 1 || c->rows > 8) return fail(MK_ERR_UNSUPPORTED, "rows must be 1..8 in this build");
-  if ((size_t)c->rows * c->n_shared * c->d_ff * 4 > (size_t)mk::kXsBytes)
+  if (c->rows < 1 || c->rows > 64) return fail(MK_ERR_UNSUPPORTED, "rows must be 1..64");
+  if (c->rows > mk::kMaxRows && (c->rows % mk::kMaxRows || c->rows_per_seq < 1 || mk::kMaxRows % c->rows_per_seq))
+    return fail(MK_ERR_UNSUPPORTED, "rows above %d must be a multiple of %d with rows_per_seq dividing %d", mk::kMaxRows,
+                mk::kMaxRows, mk::kMaxRows);
+  if ((size_t)launch_rows(*c) * c->n_shared * c->d_ff * 4 > (size_t)mk::kXsBytes)
     return fail(MK_ERR_UNSUPPORTED, "rows * n_shared * d_ff * 4 must fit %d bytes of LDS", mk::kXsBytes);
   if (c->rows_per_seq < 1 || c->rows % c->rows_per_seq) return fail(MK_ERR_INVALID_ARG, "rows_per_seq must divide rows");
   if (c->has_attn) {
@@ -156,7 +163,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   h->cfg = c;
   h->device = dev;
   h->n_cu = prop.multiProcessorCount;
-  const int M = c.rows;
+  const int M = launch_rows(c);
   const int n_seq = M / c.rows_per_seq;
   const int H = c.has_attn ? c.n_heads : 0, G = c.has_attn ? c.n_kv_heads : 0, hd = c.has_attn ? c.head_dim : 0;
   h->n_splits = 1;
@@ -298,38 +305,43 @@ int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* position
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return fail(MK_ERR_INVALID_ARG, "current device differs from the handle's device");
-  KParams p{};
-  p.L = c.n_layers; p.d = c.d_model; p.E = c.n_experts; p.k = c.top_k; p.S = c.n_shared; p.F = c.d_ff;
-  p.attn = c.has_attn ? 1 : 0;
-  p.H = c.has_attn ? c.n_heads : 0; p.G = c.has_attn ? c.n_kv_heads : 1; p.hd = c.has_attn ? c.head_dim : 0;
-  p.M = c.rows; p.rps = c.rows_per_seq; p.n_seq = n_seq;
-  p.cap = c.has_attn ? kv->capacity : 0;
-  p.kv_seqs = c.has_attn ? kv->n_seq : 0;
-  p.has_bias = c.has_router_bias ? 1 : 0;
-  p.wide = c.dtype == MK_F32 ? 1 : 0;
-  p.eps = c.rms_eps; p.theta = c.rope_theta;
-  p.n_splits = h->n_splits;
-  p.q_per_task = c.has_attn ? c.rows_per_seq * (c.n_heads / c.n_kv_heads) : 0;
-  p.n_cu = h->n_cu;
-  p.ring_tiles = h->ring_tiles;
-  p.x_bytes = h->x_bytes;
-  p.barriers = h->barriers;
-  p.timeout_ticks = 200LL * 1000 * 1000;  // 2 s of the 100 MHz realtime counter
-  p.layers = h->d_layers;
-  p.hidden_in = hidden_in;
-  p.hidden_out = hidden_out;
-  p.positions = positions;
-  p.kcache = c.has_attn ? static_cast<uint16_t*>(kv->k) : nullptr;
-  p.vcache = c.has_attn ? static_cast<uint16_t*>(kv->v) : nullptr;
-  p.act = h->d_act;
-  p.al = h->al;
-  p.sync = h->d_sync;
-  p.attn_cnt = h->d_attn_cnt;
-  p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
-  p.stamps = reinterpret_cast<long long*>(h->stamps);
-  int e = mk_launch_kernel(&p, stream);
-  if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
-  if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  const int Mg = launch_rows(c);
+  const int n_launch = c.rows / Mg;
+  for (int gi = 0; gi < n_launch; ++gi) {
+    KParams p{};
+    p.L = c.n_layers; p.d = c.d_model; p.E = c.n_experts; p.k = c.top_k; p.S = c.n_shared; p.F = c.d_ff;
+    p.attn = c.has_attn ? 1 : 0;
+    p.H = c.has_attn ? c.n_heads : 0; p.G = c.has_attn ? c.n_kv_heads : 1; p.hd = c.has_attn ? c.head_dim : 0;
+    p.M = Mg; p.rps = c.rows_per_seq; p.n_seq = Mg / c.rows_per_seq;
+    p.cap = c.has_attn ? kv->capacity : 0;
+    p.kv_seqs = c.has_attn ? kv->n_seq : 0;
+    p.row0 = gi * Mg; p.seq0 = gi * (Mg / c.rows_per_seq); p.Mt = c.rows;
+    p.has_bias = c.has_router_bias ? 1 : 0;
+    p.wide = c.dtype == MK_F32 ? 1 : 0;
+    p.eps = c.rms_eps; p.theta = c.rope_theta;
+    p.n_splits = h->n_splits;
+    p.q_per_task = c.has_attn ? c.rows_per_seq * (c.n_heads / c.n_kv_heads) : 0;
+    p.n_cu = h->n_cu;
+    p.ring_tiles = h->ring_tiles;
+    p.x_bytes = h->x_bytes;
+    p.barriers = h->barriers;
+    p.timeout_ticks = 200LL * 1000 * 1000;  // 2 s of the 100 MHz realtime counter
+    p.layers = h->d_layers;
+    p.hidden_in = hidden_in + (size_t)p.row0 * c.d_model;
+    p.hidden_out = hidden_out + (size_t)p.row0 * c.d_model;
+    p.positions = positions + p.row0;
+    p.kcache = c.has_attn ? static_cast<uint16_t*>(kv->k) : nullptr;
+    p.vcache = c.has_attn ? static_cast<uint16_t*>(kv->v) : nullptr;
+    p.act = h->d_act;
+    p.al = h->al;
+    p.sync = h->d_sync;
+    p.attn_cnt = h->d_attn_cnt;
+    p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
+    p.stamps = reinterpret_cast<long long*>(h->stamps);
+    int e = mk_launch_kernel(&p, stream);
+    if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
+    if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  }
   return MK_OK;
 }
 

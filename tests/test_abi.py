@@ -79,7 +79,9 @@ def _layers(n):
     (dict(top_k=3, n_experts=2), -2),
     (dict(n_shared=5), -2),
     (dict(rms_eps=0.0), -1),
-    (dict(rows=9), -2),
+    (dict(rows=9), -2),                # above 8 rows: a multiple of 8
+    (dict(rows=65), -2),
+    (dict(rows=16, rows_per_seq=16), -2),  # a launch of 8 rows must hold whole sequences
     (dict(rows=4, rows_per_seq=3), -1),
     (dict(has_attn=1, n_heads=3, n_kv_heads=2, head_dim=128, d_model=256, kv_capacity=16), -1),
     (dict(has_attn=1, n_heads=2, n_kv_heads=1, head_dim=64, kv_capacity=16), -2),

@@ -110,3 +110,10 @@ def test_device_generator_matches_host(env):
         else:
             ulp = np.abs(dev.astype(np.int64) - host.astype(np.int64))
         assert ulp.max() <= 1 and (ulp != 0).sum() <= 2, (dt, ulp.max(), (ulp != 0).sum())
+
+
+def test_verify_prefix_m64(env):
+    """8 sequences x 8 draft rows (a step of more than 8 rows: one launch per
+    8 rows, whole sequences each)."""
+    from synth.workloads import VERIFY92_M64
+    _run_and_check(env, VERIFY92_M64, n_layers=2)
