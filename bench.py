@@ -79,7 +79,7 @@ def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union):
     pos = np.array([[p0 + t * rows_per_seq + (r % rows_per_seq) for r in range(M)] for t in range(total)],
                    dtype=np.int32)
     pos_d = torch.as_tensor(pos, device="cuda")
-    bufs = [st.hidden(0)[:M].contiguous(), torch.empty(M, w.d, dtype=torch.float32, device="cuda")]
+    bufs = [st.hidden(0, rows=M), torch.empty(M, w.d, dtype=torch.float32, device="cuda")]
     kv = mk.mk_kv_cache(st.kc.data_ptr(), st.vc.data_ptr(), st.w.n_seq, st.w.capacity)
     ids = torch.zeros(total, st.L, M, w.k, dtype=torch.int32, device="cuda") if trace_union else None
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -204,6 +204,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="skip the 8- and 64-row verify legs")
     ap.add_argument("--cpu-layers", type=int, default=92, help="layers in the CPU-oracle sample (default: a whole step)")
     ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the workload's 92)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -252,6 +253,16 @@ def main():
         b8 = run_leg(torch, mk, st, w8, 8, 1, args.steps, args.warmup, trace_union=True)
         log(f"batch 8: {b8['ms_per_step']:.3f} ms/step, {b8['tok_s']:.1f} tok/s, {b8['achieved_gbps']:.0f} GB/s "
             f"({100 * b8['frac']:.1f}% of peak), union {b8['union_mean']:.1f}")
+    verify = {}
+    if not args.no_verify:
+        vsteps = min(args.steps, 5)
+        for M in ((8, 64) if st.w.n_seq >= 8 else (8,)):
+            wv = w8.with_(M=M, rows_per_seq=8)
+            v = run_leg(torch, mk, st, wv, M, 8, vsteps, 1, trace_union=True)
+            log(f"verify {M // 8} x 8 rows: {v['ms_per_step']:.3f} ms/step, {v['tok_s']:.1f} rows/s, "
+                f"{v['achieved_gbps']:.0f} GB/s algorithmic ({100 * v['frac']:.1f}% of peak), union {v['union_mean']:.1f}")
+            v["rows_s"] = v.pop("tok_s")
+            verify[f"verify{M}"] = {k: (round(x, 4) if isinstance(x, float) else x) for k, x in v.items()}
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -299,6 +310,7 @@ def main():
         "batch1": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b1.items()},
         "batch8": None if b8 is None else {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b8.items()},
     }
+    out.update(verify)
     print(json.dumps(out), flush=True)
 
 

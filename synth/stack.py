@@ -103,10 +103,11 @@ class DeviceStack:
                 device_normal(self.kc.data_ptr() + off, per, BF16, w.input_seed, stream_id(l, K_KCACHE, s), 0.0, 1.0)
                 device_normal(self.vc.data_ptr() + off, per, BF16, w.input_seed, stream_id(l, K_VCACHE, s), 0.0, 1.0)
 
-    def hidden(self, step=0, seed=None):
-        """Step input rows [M][d] fp32 N(0, 1), as a device tensor."""
+    def hidden(self, step=0, seed=None, rows=None):
+        """Step input rows [M][d] fp32 N(0, 1), as a device tensor (rows
+        overrides the workload's M; the first rows are the same either way)."""
         torch = _torch()
-        h = torch.empty(self.w.M, self.w.d, dtype=torch.float32, device=self.device)
+        h = torch.empty(self.w.M if rows is None else rows, self.w.d, dtype=torch.float32, device=self.device)
         device_normal(h.data_ptr(), h.numel(), F32, self.w.input_seed if seed is None else seed,
                       stream_id(-1, K_HIDDEN, step), 0.0, 1.0)
         return h
