@@ -22,7 +22,9 @@ constexpr int kLdsTotal = 160 * 1024;
 constexpr int kPartBytes = 16 * 1024;
 constexpr int kMiscBytes = 8 * 1024;
 constexpr int kXsBytes = kLdsTotal - kRing * kTileBytes - kPartBytes - kMiscBytes;  // 40 KiB
-constexpr int kPartStride = 132;        // floats per attention partial: m, l, pad, pad, acc[128]
+constexpr int kPartStride = 132;
+constexpr int kPartAcc = 3072;          // floats of GEMV partial sums in the part region
+constexpr int kResFloats = kPartBytes / 4 - kPartAcc;  // epilogue residual slice after them        // floats per attention partial: m, l, pad, pad, acc[128]
 
 // device error flag bits
 enum : unsigned { kErrTimeout = 1u, kErrPosition = 2u, kErrDupPosition = 4u };

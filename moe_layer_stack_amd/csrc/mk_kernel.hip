@@ -97,7 +97,9 @@ __device__ __forceinline__ void st_dev_u(unsigned* p, unsigned v) {
 // so for a DMA it can see it puts a full vector-memory drain in front of
 // every later LDS access, which would serialise the ring.  Here the ring's
 // waits are all explicit (wait_tiles_ahead / wait_all), and every wait is a
-// compiler memory barrier so no LDS read of a slot moves above it.
+// compiler memory barrier so no LDS read of a slot moves above it.  M0 is
+// set here and nowhere else in the kernel (no LDS DMA builtins, no
+// dynamically indexed register arrays), so the clobber cannot disturb it.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -162,7 +164,6 @@ struct Misc {
   float ssq[kWaves * kMaxRows];
   unsigned umask[kMaxExperts];                 // union expert u: rows routed to it
   signed char uslot[kMaxExperts * kMaxRows];   // [u][t]: top-k slot of expert u in row t, or -1
-  unsigned char used[kMaxExperts];
   float rope[kMaxRows * 64 * 2];  // (cos, sin) per row and frequency (head_dim 128)
   float zs[kMaxRows * kMaxExperts];  // router logits of the step's rows
 };
@@ -738,13 +739,16 @@ __device__ __forceinline__ void seg_all(Seg<MT>& sg, int M) {
 // 2^lrb-byte rows is (wave*2048 + c*1024) >> lrb.
 template <int MT>
 __device__ __forceinline__ float part_row(const float* part, int block, int q, int lrb, int t) {
+  // row q of 2^lrb-byte rows (>= 1 KiB) covers chunks q*cpr .. q*cpr+cpr-1;
+  // all 8 chunks are read (no branches between the LDS reads) and masked
   const float* b = part + (size_t)block * (kWaves * 2 * MT);
+  const int cpr = 1 << (lrb - 10), c0 = q * cpr;
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      if (((w * 2048 + c * 1024) >> lrb) == q) s += b[(w * 2 + c) * MT + t];
+  for (int ch = 0; ch < kWaves * 2; ++ch) {
+    const float v = b[ch * MT + t];
+    s += (ch >= c0 && ch < c0 + cpr) ? v : 0.f;
+  }
   return s;
 }
 
@@ -784,8 +788,6 @@ __device__ __forceinline__ void run_gemv(Smem sm, Stream& st, const Plan& cur, c
 // The part region holds the GEMV accumulators (kPartAcc floats) followed by
 // the residual slice (kResFloats) an epilogue adds: epilogues read it from
 // LDS because a global load there would wait behind the ring's loads.
-constexpr int kPartAcc = 3072;
-constexpr int kResFloats = kPartBytes / 4 - kPartAcc;
 __device__ __forceinline__ float* res_slice(Smem sm) { return sm.part + kPartAcc; }
 __device__ __forceinline__ void zero_part(Smem sm) {
   for (int i = threadIdx.x; i < kPartAcc; i += kThreads) sm.part[i] = 0.f;
@@ -962,21 +964,42 @@ __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, 
   }
 }
 
-// max over the four 16-lane rows (lanes with equal bits 0-3), in every lane
-__device__ __forceinline__ float max_rows(float v) {
+// Lane groups used by the decode attention: lane l covers position l >> 3
+// of the wave's 8 and dims 16 * (l & 7) .. +16.
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: i <-> 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;      // row_mirror: i <-> 15 - i within 16 lanes
+// sum over the 8 lanes of a position group (lane bits 0-2), in every lane
+__device__ __forceinline__ float sum_oct(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);  // values are uniform within quads here
+  return v;
+}
+// max over the 8 position groups of a value uniform within each group
+__device__ __forceinline__ float max_groups(float v) {
+  v = fmaxf(v, dpp<kDppMirror>(v));  // uniform within 8-lane groups: the mirror is the other group
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// sum over the 8 position groups (lane bits 3-5) of a per-lane value, in every lane
+__device__ __forceinline__ float sum_groups(float v) {
+  v += dpp<kDppRor8>(v);  // lane bit 3
+  return sum_rows(v);     // lane bits 4, 5
 }
 
 // Split-KV GQA decode attention for tasks of at most NQ query vectors
 // (sequence rows * heads per kv head).  Task = (sequence, kv head, split) =
-// this CU.  The split streams as K, V tile pairs of 32 positions; wave w
-// takes positions 8w .. 8w+7 of every tile (its 2 KiB quarter, as in a GEMV
-// tile), a lane covering 8 dims (lane & 15) of one position per 1 KiB chunk,
-// for every query.  Each wave keeps an online-softmax state per query; the
-// four are merged through LDS into the split's partial.
+// this CU; the split's positions are spread over the splits tile by tile.
+// The split streams as K, V tile pairs of 32 positions; wave w takes
+// positions 8w .. 8w+7 of every tile (its 2 KiB quarter, as in a GEMV tile),
+// lane l covering 16 dims (16 * (l & 7)) of position l >> 3, for every query.
+// Scores are kept in log2 units (q is prescaled by log2(e) / sqrt(hd)) so
+// that exp2 applies directly; each wave keeps an online-softmax state per
+// query and rescales its sums only when the running maximum grows by more
+// than 8 (probabilities stay below 2^8).  The four wave states are merged
+// through LDS into the split's partial (maximum stored in natural units).
 template <int NQ>
 __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l, Stream& st, const Plan& P,
                                                const Plan& N) {
@@ -996,106 +1019,150 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   const int p_lo = P.a0, p_hi = P.a1;
   if (active) attn_prologue(p, ms, l, seq, g, Q, p_lo, p_hi, P, Qv, newk, newv);
   __syncthreads();
-  const int d0 = (lane & 15) * 8, prow = lane >> 4;
+  const int d0 = (lane & 7) * 16, pgrp = lane >> 3;
+  constexpr float kLog2e = 1.4426950408889634f;
+  // Set-up reads are unconditional (every index stays inside its array) and
+  // masked by selects: conditional LDS reads would each wait a round trip.
+  // This step's rows inside the split: their positions (uniform), and the span.
   int newpos[kMaxRows];
+  int new_lo = 1 << 30, new_hi = -1;
 #pragma unroll
   for (int rr = 0; rr < kMaxRows; ++rr) {
-    newpos[rr] = -1;
-    if (active && rr < rps) {
-      const int pos = ms->pos[seq * rps + rr];
-      if (pos >= p_lo && pos < p_hi) newpos[rr] = pos;
-    }
+    const int pos = ms->pos[min(seq * rps + rr, kMaxRows - 1)];
+    const bool in = active & (rr < rps) & (pos >= p_lo) & (pos < p_hi);
+    newpos[rr] = in ? pos : -1;
+    new_lo = in ? min(new_lo, pos) : new_lo;
+    new_hi = in ? max(new_hi, pos) : new_hi;
   }
-  float qr[NQ][8], acc[NQ][8], m[NQ], lsum[NQ], pp[NQ][2];
+  float qr[NQ][16], acc[NQ][16], m[NQ], lsum[NQ], pq[NQ];
   int qlim[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
+    const bool qok = active & (q < Q);
+    const float4* src = reinterpret_cast<const float4*>(Qv + q * 128 + d0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[q][e] = 0.f;
-      qr[q][e] = (active && q < Q) ? Qv[q * 128 + d0 + e] : 0.f;
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const float4 a = src[e4];
+      qr[q][4 * e4 + 0] = qok ? a.x * kLog2e : 0.f;
+      qr[q][4 * e4 + 1] = qok ? a.y * kLog2e : 0.f;
+      qr[q][4 * e4 + 2] = qok ? a.z * kLog2e : 0.f;
+      qr[q][4 * e4 + 3] = qok ? a.w * kLog2e : 0.f;
     }
-    pp[q][0] = pp[q][1] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
+    pq[q] = 0.f;
     m[q] = -INFINITY;
     lsum[q] = 0.f;
-    qlim[q] = (active && q < Q) ? min(p_hi - 1, ms->pos[seq * rps + q / HG]) : -1;  // last visible position
+    const int rowpos = ms->pos[min(seq * rps + q / HG, kMaxRows - 1)];
+    qlim[q] = qok ? min(p_hi - 1, rowpos) : -1;  // last visible position
   }
   st.mark(1);
   settle();
   st.fill(sm, P, N, 0, wave, lane);
   for (int i = 0; i < P.n; ++i) {
     st.wait(i);
-    const char* sl = st.slot(sm, i) + wave * 2048 + lane * 16;
+    const char* sl = st.slot(sm, i) + wave * 2048 + pgrp * 256 + d0 * 2;
     const uint4 raw0 = *reinterpret_cast<const uint4*>(sl);
-    const uint4 raw1 = *reinterpret_cast<const uint4*>(sl + 1024);
+    const uint4 raw1 = *reinterpret_cast<const uint4*>(sl + 16);
     const int t0 = p_lo + (i >> 1) * kAttnTile;
     const bool is_v = (i & 1) != 0;
-    float f[2][8];
-    unpack16<uint16_t>(raw0, f[0]);
-    unpack16<uint16_t>(raw1, f[1]);
-    int jpos[2];
+    const int jpos = t0 + wave * 8 + pgrp;
+    float f[16];
+    unpack16<uint16_t>(raw0, f);
+    unpack16<uint16_t>(raw1, f + 8);
+    if (new_lo <= t0 + kAttnTile - 1 && new_hi >= t0) {  // a row written this step lies in the tile
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      jpos[c] = t0 + wave * 8 + c * 4 + prow;
-#pragma unroll
-      for (int rr = 0; rr < kMaxRows; ++rr) {
-        if (newpos[rr] == jpos[c]) {
+      for (int rr = 0; rr < kMaxRows; ++rr) {  // newpos[rr] is -1 for rr >= rps
+        if (newpos[rr] == jpos) {
           const float* src = (is_v ? newv : newk) + rr * 128 + d0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[c][e] = src[e];
+          for (int e = 0; e < 16; ++e) f[e] = src[e];
         }
       }
     }
     if (!is_v) {
+      // all queries in lockstep (no branch between their chains)
+      float sc[NQ], mt[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        float sc[2];
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            a0 = fmaf(f[c][e], qr[q][e], a0);
-            a1 = fmaf(f[c][e + 1], qr[q][e + 1], a1);
-          }
-          const float dsum = sum_row16(a0 + a1);
-          sc[c] = (jpos[c] <= qlim[q]) ? dsum : -INFINITY;
+        for (int e = 0; e < 16; e += 2) {
+          a0 = fmaf(f[e], qr[q][e], a0);
+          a1 = fmaf(f[e + 1], qr[q][e + 1], a1);
         }
-        const float mt = max_rows(fmaxf(sc[0], sc[1]));
-        const float mn = fmaxf(m[q], mt);
-        const float corr = (mn == -INFINITY) ? 1.f : __expf(m[q] - mn);
+        sc[q] = (jpos <= qlim[q]) ? sum_oct(a0 + a1) : -INFINITY;
+      }
+      bool raise = false;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) pp[q][c] = (sc[c] == -INFINITY) ? 0.f : __expf(sc[c] - mn);
-        lsum[q] = lsum[q] * corr + pp[q][0] + pp[q][1];
-        m[q] = mn;
+      for (int q = 0; q < NQ; ++q) {
+        mt[q] = max_groups(sc[q]);
+        raise |= mt[q] > m[q] + 8.f;
+      }
+      if (raise) {  // wave-uniform and rare: raise the reference maxima
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[q][e] *= corr;
+        for (int q = 0; q < NQ; ++q) {
+          const bool up = mt[q] > m[q] + 8.f;
+          const float corr = (!up) ? 1.f : (m[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[q] - mt[q]);
+          lsum[q] *= corr;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[q][e] *= corr;
+          m[q] = up ? mt[q] : m[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        pq[q] = (sc[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[q] - m[q]);
+        lsum[q] += pq[q];
       }
     } else {
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(pp[q][0], f[0][e], fmaf(pp[q][1], f[1][e], acc[q][e]));
+        for (int e = 0; e < 16; ++e) acc[q][e] = fmaf(pq[q], f[e], acc[q][e]);
     }
     st.fill(sm, P, N, i + 1, wave, lane);
   }
   st.mark(2);
   if (!active) return;
-  // wave states: lsum and acc summed over the wave's 4 position rows (each
-  // row's 16 lanes hold the same p, so one lane per row counts)
+  // Wave states.  acc[q][e] is summed over the 8 position groups (lane bits
+  // 3-5) by a reduce-scatter: after halving over bits 5, 4 and 3 a lane
+  // holds, for query 2*b5 + b4, the 8 dims 16*(lane & 7) + 8*b3 + 0..7.
+  // lsum is uniform within a group, so its sum over the groups counts each
+  // position once.
+  constexpr float kLn2 = 0.6931471805599453f;
+  static_assert(NQ == 4, "the reduce-scatter below is written for 4 queries");
+  {
+    float v[64];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[q * 16 + e] = acc[q][e];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = swap32_sum(v[i], v[32 + i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = swap16_sum(v[i], v[16 + i]);
+    const bool b3 = (lane >> 3) & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float mine = b3 ? v[8 + i] : v[i];
+      const float other = b3 ? v[i] : v[8 + i];
+      v[i] = mine + dpp<kDppRor8>(other);
+    }
+    const int q = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+    if (q < Q) {
+      float* dst = wst + (size_t)(wave * NQ + q) * kPartStride + 4 + d0 + 8 * (int)b3;
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const float lw = sum_rows(lsum[q]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[q][e] = sum_rows(acc[q][e]);
-    if (q < Q && lane < 16) {
+    const float lw = sum_groups(lsum[q]);
+    if (q < Q && lane == 0) {
       float* dst = wst + (size_t)(wave * NQ + q) * kPartStride;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[4 + d0 + e] = acc[q][e];
-      if (lane == 0) {
-        dst[0] = m[q];
-        dst[1] = lw;
-      }
+      dst[0] = m[q] == -INFINITY ? -INFINITY : m[q] * kLn2;  // natural units
+      dst[1] = lw;
     }
   }
   __syncthreads();
@@ -1411,13 +1478,6 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
       });
 }
 
-// slot of expert e in row t's top-k list, or -1
-__device__ __forceinline__ int slot_of(const Misc* ms, int t, int k, int e) {
-  for (int i = 0; i < k; ++i)
-    if (ms->ids[t * k + i] == e) return i;
-  return -1;
-}
-
 // Top-k over the router logits of every row (all CUs, redundantly), then the
 // union of chosen experts.  Selection is on the logits, larger first, equal
 // logits ranked by lower expert id; weights are softmax probabilities
@@ -1427,12 +1487,14 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
   const int E = p.E, k = p.k, M = p.M;
   const float* logits = act_f(p, l, p.al.logits);
   Misc* ms = sm.misc;
-  for (int e = threadIdx.x; e < kMaxExperts; e += kThreads) ms->used[e] = 0;
   for (int it = threadIdx.x; it < M * kMaxExperts; it += kThreads) {
     const int t = it / kMaxExperts, e = it % kMaxExperts;
     ms->zs[it] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
   }
   __syncthreads();
+  // rank[t][e]: top-k slot of expert e in row t, or -1 (written over the
+  // staged logits of row t once this wave has read them)
+  int* rank_tab = reinterpret_cast<int*>(ms->zs);
   for (int t = wave; t < M; t += kWaves) {
     // lane e: rank of expert e among the row's logits (larger first, equal
     // logits by lower id), from broadcast reads of the staged row
@@ -1450,28 +1512,36 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
     const bool sel = lane < E && rank < k;
     const float pz = sel ? __expf(z - zmax) : 0.f;
     const float psum = sum_rows(sum_row16(pz));
+    rank_tab[t * kMaxExperts + lane] = sel ? rank : -1;
     if (sel) {
       ms->ids[t * k + rank] = lane;
       ms->wts[t * k + rank] = pz / psum;
-      ms->used[lane] = 1;
     }
   }
   __syncthreads();
+  // union of the rows' experts (ascending ids), read without branches
   if (wave == 0) {
-    const bool u = lane < E && ms->used[lane];
+    bool u = false;
+#pragma unroll
+    for (int t = 0; t < kMaxRows; ++t) u |= (t < M) & (rank_tab[t * kMaxExperts + lane] >= 0);
     const unsigned long long mm = __ballot(u);
     if (u) ms->uni[__popcll(mm & ((1ull << lane) - 1ull))] = lane;
     if (lane == 0) ms->n_uni = __popcll(mm);
   }
   __syncthreads();
-  for (int u = threadIdx.x; u < ms->n_uni; u += kThreads) {
-    const int e = ms->uni[u];
+  const int n_uni = ms->n_uni;
+  for (int it = threadIdx.x; it < kMaxExperts * kMaxRows; it += kThreads) {
+    const int u = it / kMaxRows, t = it % kMaxRows;
+    const int e = ms->uni[u] & (kMaxExperts - 1);
+    const int r = rank_tab[t * kMaxExperts + e];
+    ms->uslot[it] = (signed char)((u < n_uni && t < M) ? r : -1);
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < kMaxExperts; u += kThreads) {
+    const signed char* us = ms->uslot + u * kMaxRows;
     unsigned m = 0;
-    for (int t = 0; t < M; ++t) {
-      const int sl = slot_of(ms, t, k, e);
-      ms->uslot[u * kMaxRows + t] = (signed char)sl;
-      if (sl >= 0) m |= 1u << t;
-    }
+#pragma unroll
+    for (int t = 0; t < kMaxRows; ++t) m |= (us[t] >= 0 ? 1u : 0u) << t;
     ms->umask[u] = m;
   }
   __syncthreads();
@@ -1494,17 +1564,22 @@ __device__ __forceinline__ void load_x_lds(XRegs<WT, MT>& xr, const float* base,
   for (int c = 0; c < 2; ++c) {
     const int k0 = lane_k0<WT>(wave, lane, c, lrb);
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      if (tm & (1u << t)) {
-        const float* s = base + rowoff[t] + k0;
+    for (int t = 0; t < MT; ++t) {  // every row offset is valid; tm masks the arithmetic
+      const float* s = base + rowoff[t] + k0;
 #pragma unroll
-        for (int j = 0; j < EPL; j += 4) {
-          const float4 a4 = *reinterpret_cast<const float4*>(s + j);
-          xr.v[t][c][j] = a4.x; xr.v[t][c][j + 1] = a4.y; xr.v[t][c][j + 2] = a4.z; xr.v[t][c][j + 3] = a4.w;
-        }
+      for (int j = 0; j < EPL; j += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(s + j);
+        xr.v[t][c][j] = a4.x; xr.v[t][c][j + 1] = a4.y; xr.v[t][c][j + 2] = a4.z; xr.v[t][c][j + 3] = a4.w;
       }
     }
   }
+}
+
+// Shared activations a_s [M][S][F] -> LDS by DMA (whole KiB; F*4 bytes is a
+// multiple of 1 KiB), issued right after the RS -> RG barrier so that its
+// latency overlaps the routing step's load of the logits.
+__device__ __forceinline__ void rg_stage(const KParams& p, Smem sm, int l) {
+  dma_to_lds((char*)sm.xs, (const char*)act_f(p, l, p.al.a_s), p.M * p.S * p.F * 4, wave_id(), threadIdx.x & 63);
 }
 
 // RG: shared-expert down projection y_s = sum_s Wd_s a_s (x from LDS), then
@@ -1515,12 +1590,10 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
                                          const XRegs<WT, MT>& xr) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int d = p.d, F = p.F, k = p.k, M = p.M, S = p.S;
-  const float* as_g = act_f(p, l, p.al.a_s);
   float* a = act_w(p, l, p.al.a);
   float* ys = act_w(p, l, p.al.y_s);
-  // misc->rinv still holds RS's 1/rms of h1.  Shared activations a_s
-  // [M][S][F] -> LDS by DMA (whole KiB; F*4 bytes is a multiple of 1 KiB).
-  dma_to_lds((char*)sm.xs, (const char*)as_g, M * S * F * 4, wave, lane);
+  // misc->rinv still holds RS's 1/rms of h1; the shared activations are on
+  // their way to LDS (rg_stage, issued before the routing step).
   zero_part(sm);
   wait_all();
   __syncthreads();
@@ -1616,17 +1689,13 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
         unsigned tm = 0;
         int ro[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          sg.tw[t] = 0.f;
-          ro[t] = 0;
-          if (t < M) {
-            const int sl = ms->uslot[u * kMaxRows + t];
-            if (sl >= 0) {
-              ro[t] = (t * k + sl) * F;
-              sg.tw[t] = ms->wts[t * k + sl];
-              tm |= 1u << t;
-            }
-          }
+        for (int t = 0; t < MT; ++t) {  // uslot is -1 for rows beyond M
+          const int sl = ms->uslot[u * kMaxRows + t];
+          const int slc = sl < 0 ? 0 : sl;
+          const float wt = ms->wts[min(t * k + slc, kMaxRows * kMaxTopK - 1)];
+          ro[t] = sl < 0 ? 0 : (t * k + sl) * F;
+          sg.tw[t] = sl < 0 ? 0.f : wt;
+          tm |= (sl < 0 ? 0u : 1u) << t;
         }
         load_x_lds<WT, MT>(xr, xl ? sm.xs : a_g, ro, tm, wave, lane, lrb);
         sg.tmask = tm;
@@ -1739,6 +1808,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
       st.advance(cur);
     }
     {
+      rg_stage(p, sm, l);
       route_topk(p, sm, l);
       cur = plan_rg<WT>(p, ms, l, true);  // same first tiles as the prefetched plan
       const Plan nxt = plan_down<WT>(p, ms, l);

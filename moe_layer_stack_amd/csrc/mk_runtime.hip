@@ -176,7 +176,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   }
   {
     // epilogue residual slices (output columns of one CU, every row) live in
-    // 1024 floats of LDS
+    // kResFloats floats of LDS
     const int esz = c.dtype == MK_BF16 ? 2 : 4;
     auto cols = [&](int row_elems) {
       const int rpt = mk::kTileBytes / (row_elems * esz);
@@ -185,7 +185,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
     };
     int ncol = cols(c.d_ff);
     if (c.has_attn && cols(c.n_heads * c.head_dim) > ncol) ncol = cols(c.n_heads * c.head_dim);
-    if (ncol * M > 1024) {
+    if (ncol * M > mk::kResFloats) {
       delete h;
       return fail(MK_ERR_UNSUPPORTED, "d_model * rows too large for %d CUs", prop.multiProcessorCount);
     }
