@@ -1492,31 +1492,54 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
     ms->zs[it] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
   }
   __syncthreads();
-  // rank[t][e]: top-k slot of expert e in row t, or -1 (written over the
-  // staged logits of row t once this wave has read them)
-  int* rank_tab = reinterpret_cast<int*>(ms->zs);
-  for (int t = wave; t < M; t += kWaves) {
-    // lane e: rank of expert e among the row's logits (larger first, equal
-    // logits by lower id), from broadcast reads of the staged row
-    const float* zr = ms->zs + t * kMaxExperts;
-    const float z = zr[lane];
-    int rank = 0;
-    float zmax = -INFINITY;
+  // rank[t][e]: top-k slot of expert e in row t, or -1.  Kept in the
+  // epilogue residual slice of the part region, which is free until DOWN.
+  int* rank_tab = reinterpret_cast<int*>(res_slice(sm));
+  static_assert(kMaxRows * kMaxExperts <= kResFloats, "rank table does not fit");
+  // Thread (e, part): expert e against the quarter `part` of the row's
+  // logits; the four partial ranks and maxima meet in the lane quad.
+  {
+    const int e = threadIdx.x >> 2, part = threadIdx.x & 3;
+    for (int t = 0; t < M; ++t) {
+      const float* zr = ms->zs + t * kMaxExperts;
+      const float z = zr[e];
+      int r = 0;
+      float zm = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kMaxExperts; j += 4) {
-      const float4 o = *reinterpret_cast<const float4*>(zr + j);
-      rank += (o.x > z || (o.x == z && j < lane)) + (o.y > z || (o.y == z && j + 1 < lane)) +
-              (o.z > z || (o.z == z && j + 2 < lane)) + (o.w > z || (o.w == z && j + 3 < lane));
-      zmax = fmaxf(zmax, fmaxf(fmaxf(o.x, o.y), fmaxf(o.z, o.w)));
+      for (int jj = 0; jj < kMaxExperts / 4; jj += 4) {
+        const int j = part * (kMaxExperts / 4) + jj;
+        const float4 o = *reinterpret_cast<const float4*>(zr + j);
+        const int dd = e - j;  // expert j + c ranks first on a tie when c < dd
+        r += (o.x > z || (o.x == z && 0 < dd)) + (o.y > z || (o.y == z && 1 < dd)) +
+             (o.z > z || (o.z == z && 2 < dd)) + (o.w > z || (o.w == z && 3 < dd));
+        zm = fmaxf(zm, fmaxf(fmaxf(o.x, o.y), fmaxf(o.z, o.w)));
+      }
+      r += __builtin_amdgcn_update_dpp(0, r, kDppXor1, 0xF, 0xF, false);
+      r += __builtin_amdgcn_update_dpp(0, r, kDppXor2, 0xF, 0xF, false);
+      zm = fmaxf(zm, dpp<kDppXor1>(zm));
+      zm = fmaxf(zm, dpp<kDppXor2>(zm));
+      const bool sel = e < E && r < k;
+      if (part == 0) {
+        rank_tab[t * kMaxExperts + e] = sel ? r : -1;
+        if (sel) {
+          ms->ids[t * k + r] = e;
+          ms->wts[t * k + r] = __expf(z - zm);  // normalised below
+        }
+      }
     }
-    const bool sel = lane < E && rank < k;
-    const float pz = sel ? __expf(z - zmax) : 0.f;
-    const float psum = sum_rows(sum_row16(pz));
-    rank_tab[t * kMaxExperts + lane] = sel ? rank : -1;
-    if (sel) {
-      ms->ids[t * k + rank] = lane;
-      ms->wts[t * k + rank] = pz / psum;
+  }
+  __syncthreads();
+  // renormalise over the chosen set: w = p_e / sum_{top-k} p
+  {
+    const int t = threadIdx.x / kMaxTopK, i = threadIdx.x % kMaxTopK;
+    float w = 0.f, psum = 0.f;
+    if (t < M && i < k) {
+      w = ms->wts[t * k + i];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) psum += (j < k) ? ms->wts[t * k + min(j, k - 1)] : 0.f;
     }
+    __syncthreads();
+    if (t < M && i < k) ms->wts[t * k + i] = w / psum;
   }
   __syncthreads();
   // union of the rows' experts (ascending ids), read without branches
