@@ -349,7 +349,11 @@ __device__ __forceinline__ Plan plan_qkv(const KParams& p, int l) {
 }
 
 // attention split owned by this CU (tasks never outnumber CUs)
-__device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int l) {
+// trail: one row per sequence (decode); its new position, the sequence's
+// last, is attended from the copy in LDS instead of a cache tile, and the
+// split S-1 owns it (P.U = 1, P.F = its position).  The cached positions are
+// spread over the splits tile by tile.
+__device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int l, bool trail) {
   Plan P{};
   P.kind = PK_ATTN;
   const int S = p.n_splits;
@@ -358,12 +362,15 @@ __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int 
   const int seq = task / (p.G * S), g = (task / S) % p.G, s = task % S;
   int maxpos = 0;
   for (int rr = 0; rr < p.rps; ++rr) maxpos = max(maxpos, ms->pos[seq * p.rps + rr]);
-  const int npos = maxpos + 1;
-  int sl = (npos + S - 1) / S;
-  sl = (sl + kAttnTile - 1) / kAttnTile * kAttnTile;
-  P.a0 = s * sl;
-  P.a1 = min(P.a0 + sl, npos);
-  P.n = P.a1 > P.a0 ? 2 * ((P.a1 - P.a0 + kAttnTile - 1) / kAttnTile) : 0;
+  const bool tr = trail && p.rps == 1;
+  const int npos = tr ? maxpos : maxpos + 1;  // positions read from the cache
+  const int ntile = (npos + kAttnTile - 1) / kAttnTile;
+  const int t_lo = (int)(((long long)s * ntile) / S), t_hi = (int)(((long long)(s + 1) * ntile) / S);
+  P.a0 = min(t_lo * kAttnTile, npos);
+  P.a1 = min(t_hi * kAttnTile, npos);
+  P.n = 2 * (t_hi - t_lo);
+  P.U = (tr && s == S - 1) ? 1 : 0;
+  P.F = maxpos;
   const size_t kv_base = ((((size_t)l * p.kv_seqs + p.seq0 + seq) * p.G + g) * (size_t)p.cap) * p.hd;
   P.b0 = reinterpret_cast<const char*>(p.kcache + kv_base);
   P.b1 = reinterpret_cast<const char*>(p.vcache + kv_base);
@@ -927,6 +934,7 @@ __device__ __forceinline__ void attn_combine(const KParams& p, Smem sm, int l, i
 __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, int l, int seq, int g, int Q,
                                               int p_lo, int p_hi, const Plan& P, float* Qv, float* newk,
                                               float* newv) {
+  if (P.U) p_hi = P.F + 1;  // this split also writes the trailing row
   const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
   const int nrows_qkv = (p.H + 2 * p.G) * hd;
   const float* qkv = act_f(p, l, p.al.qkv);
@@ -1035,7 +1043,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
     new_hi = in ? max(new_hi, pos) : new_hi;
   }
   float qr[NQ][16], acc[NQ][16], m[NQ], lsum[NQ], pq[NQ];
-  int qlim[NQ];
+  int qlim[NQ], qvis[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const bool qok = active & (q < Q);
@@ -1054,8 +1062,53 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
     m[q] = -INFINITY;
     lsum[q] = 0.f;
     const int rowpos = ms->pos[min(seq * rps + q / HG, kMaxRows - 1)];
-    qlim[q] = qok ? min(p_hi - 1, rowpos) : -1;  // last visible position
+    qvis[q] = qok ? rowpos : -1;         // last position the query sees
+    qlim[q] = min(p_hi - 1, qvis[q]);    // ... among the split's tiles
   }
+  // One K row (scores, online-softmax update) and one V row (accumulation)
+  // of the wave's 8 positions; jpos is this lane's position.
+  auto k_row = [&](const float (&f)[16], int jpos, const int (&lim)[NQ]) __attribute__((always_inline)) {
+    // all queries in lockstep (no branch between their chains)
+    float sc[NQ], mt[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        a0 = fmaf(f[e], qr[q][e], a0);
+        a1 = fmaf(f[e + 1], qr[q][e + 1], a1);
+      }
+      sc[q] = (jpos <= lim[q]) ? sum_oct(a0 + a1) : -INFINITY;
+    }
+    bool raise = false;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      mt[q] = max_groups(sc[q]);
+      raise |= mt[q] > m[q] + 8.f;
+    }
+    if (raise) {  // wave-uniform and rare: raise the reference maxima
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const bool up = mt[q] > m[q] + 8.f;
+        const float corr = (!up) ? 1.f : (m[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[q] - mt[q]);
+        lsum[q] *= corr;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[q][e] *= corr;
+        m[q] = up ? mt[q] : m[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      pq[q] = (sc[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[q] - m[q]);
+      lsum[q] += pq[q];
+    }
+  };
+  auto v_row = [&](const float (&f)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[q][e] = fmaf(pq[q], f[e], acc[q][e]);
+  };
   st.mark(1);
   settle();
   st.fill(sm, P, N, 0, wave, lane);
@@ -1080,48 +1133,20 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
         }
       }
     }
-    if (!is_v) {
-      // all queries in lockstep (no branch between their chains)
-      float sc[NQ], mt[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          a0 = fmaf(f[e], qr[q][e], a0);
-          a1 = fmaf(f[e + 1], qr[q][e + 1], a1);
-        }
-        sc[q] = (jpos <= qlim[q]) ? sum_oct(a0 + a1) : -INFINITY;
-      }
-      bool raise = false;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        mt[q] = max_groups(sc[q]);
-        raise |= mt[q] > m[q] + 8.f;
-      }
-      if (raise) {  // wave-uniform and rare: raise the reference maxima
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const bool up = mt[q] > m[q] + 8.f;
-          const float corr = (!up) ? 1.f : (m[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[q] - mt[q]);
-          lsum[q] *= corr;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[q][e] *= corr;
-          m[q] = up ? mt[q] : m[q];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        pq[q] = (sc[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[q] - m[q]);
-        lsum[q] += pq[q];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[q][e] = fmaf(pq[q], f[e], acc[q][e]);
-    }
+    if (!is_v)
+      k_row(f, jpos, qlim);
+    else
+      v_row(f);
     st.fill(sm, P, N, i + 1, wave, lane);
+  }
+  if (P.U && wave == 0) {  // the trailing row, from its copy in LDS: position group 0 of wave 0
+    float f[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = newk[d0 + e];
+    k_row(f, pgrp == 0 ? P.F : (1 << 30), qvis);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = newv[d0 + e];
+    v_row(f);
   }
   st.mark(2);
   if (!active) return;
@@ -1802,7 +1827,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   for (int l = 0; l < p.L; ++l) {
     if (p.attn) {
       {
-        const Plan nxt = plan_attn(p, ms, l);
+        const Plan nxt = plan_attn(p, ms, l, QW == 1);
         phase_qkv<WT, MT>(p, sm, l, st, cur, nxt);
         MK_SYNC();
         st.advance(cur);
