@@ -723,6 +723,42 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
   }
 }
 
+// One row per step: this wave's quarter of the g <= G tiles i .. i+g-1
+// against x, each chunk's dot product scaled by tw and added to the lane's
+// running sums pacc[u*2 + c] (no cross-lane reduction here).
+template <typename WT>
+__device__ __forceinline__ void gemv_acc1(Smem sm, const Stream& st, int i, int g, const XRegs<WT, 1>& xr, float tw,
+                                          float (&pacc)[GroupOf<1>::G * 2], int wave, int lane) {
+  constexpr int G = GroupOf<1>::G;
+  constexpr int EPL = XRegs<WT, 1>::EPL;
+  uint4 wv[G][2];
+  const int rs0 = (st.slot0 + i) % kRing;
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    if (u < g) {
+      const int rs = rs0 + u < kRing ? rs0 + u : rs0 + u - kRing;
+      const char* sl = sm.ring + (size_t)rs * kTileBytes + wave * 2048 + lane * 16;
+      wv[u][0] = *reinterpret_cast<const uint4*>(sl);
+      wv[u][1] = *reinterpret_cast<const uint4*>(sl + 1024);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float w[EPL];
+      unpack16<WT>(wv[u][c], w);
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; j += 2) {
+        s0 = fmaf(w[j], xr.v[0][c][j], s0);
+        s1 = fmaf(w[j + 1], xr.v[0][c][j + 1], s1);
+      }
+      if (u < g) pacc[u * 2 + c] = fmaf(s0 + s1, tw, pacc[u * 2 + c]);
+    }
+  }
+}
+
 // A run of tiles that share x registers, token mask and weights, with
 // consecutive part blocks starting at blk0; the loop calls the phase's
 // epilogue after the run when round_end is set.
@@ -750,12 +786,16 @@ __device__ __forceinline__ float part_row(const float* part, int block, int q, i
   // all 8 chunks are read (no branches between the LDS reads) and masked
   const float* b = part + (size_t)block * (kWaves * 2 * MT);
   const int cpr = 1 << (lrb - 10), c0 = q * cpr;
+  float v[kWaves * 2];
+#pragma unroll
+  for (int ch = 0; ch < kWaves * 2; ++ch) v[ch] = b[ch * MT + t];
+  // One use of all eight values before the selects: otherwise the compiler
+  // moves each read under its select's branch and the reads run one after
+  // another, a full LDS round trip each.
+  asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
   float s = 0.f;
 #pragma unroll
-  for (int ch = 0; ch < kWaves * 2; ++ch) {
-    const float v = b[ch * MT + t];
-    s += (ch >= c0 && ch < c0 + cpr) ? v : 0.f;
-  }
+  for (int ch = 0; ch < kWaves * 2; ++ch) s += (ch >= c0 && ch < c0 + cpr) ? v[ch] : 0.f;
   return s;
 }
 
@@ -1729,6 +1769,61 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
   __syncthreads();
   const Misc* ms = sm.misc;
   const float* res = res_slice(sm);
+  auto epilogue = [&](int, int) {
+    for (int it = threadIdx.x; it < ncol * M; it += kThreads) {
+      const int q = MT == 1 ? it : it / M, t = MT == 1 ? 0 : it - q * M;
+      const int j = lo * rpt + q;
+      const float out = res[t * ncol + q] + part_row<MT>(sm.part, q >> (13 - lrb), q & (rpt - 1), lrb, t);
+      if (last_layer) h2[(size_t)t * d + j] = out;
+      else st_dev(h2 + (size_t)t * d + j, out);
+    }
+  };
+  if constexpr (MT == 1) {
+    constexpr int G = GroupOf<1>::G;
+    if (nj <= G && xl) {
+      // One row: the union experts are its k experts, each expert's j-blocks
+      // form one group, and the weighted partial sums of all experts stay in
+      // registers until one cross-lane reduction at the end.  The next
+      // expert's x registers are read from LDS while the current expert's
+      // tiles are consumed.  Lane u < U holds expert u's x offset and weight.
+      const int U = P.U;
+      const int su = ms->uslot[(lane & (kMaxTopK - 1)) * kMaxRows];
+      const int sc = su < 0 ? 0 : su;
+      const int xoff_l = sc * F;
+      const float wt_l = ms->wts[sc];
+      XRegs<WT, 1> xa, xb;
+      auto ldx = [&](XRegs<WT, 1>& x, int u) {
+        const int ro[1] = {__builtin_amdgcn_readlane(xoff_l, u)};
+        load_x_lds<WT, 1>(x, sm.xs, ro, 1u, wave, lane, lrb);
+      };
+      float pacc[G * 2];
+#pragma unroll
+      for (int v = 0; v < G * 2; ++v) pacc[v] = 0.f;
+      st.mark(1);
+      settle();
+      st.fill(sm, P, N, 0, wave, lane);
+      ldx(xa, 0);
+      for (int u = 0; u < (nj > 0 ? U : 0); ++u) {
+        if (u + 1 < U) ldx(xb, u + 1);
+        const float tw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt_l), u));
+        const int j = u * nj;
+        st.wait(j + nj - 1);
+        gemv_acc1<WT>(sm, st, j, nj, xa, tw, pacc, wave, lane);
+        st.fill(sm, P, N, j + nj, wave, lane);
+        xa = xb;
+      }
+      const float r = xreduce<G * 2>(pacc, lane);
+      if (xreduce_writer<G * 2>(lane)) {
+        const int idx = xreduce_index<G * 2>(lane);
+        if (idx / 2 < nj) sm.part[(idx / 2) * (kWaves * 2) + wave * 2 + (idx & 1)] = r;
+      }
+      __syncthreads();
+      epilogue(0, n - 1);
+      __syncthreads();
+      st.mark(2);
+      return;
+    }
+  }
   XRegs<WT, MT> xr;
   run_gemv<WT, MT>(
       sm, st, P, N, xr,
@@ -1752,15 +1847,7 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
         sg.accum = true;
         sg.round_end = sg.end == n;
       },
-      [&](int, int) {
-        for (int it = threadIdx.x; it < ncol * M; it += kThreads) {
-          const int q = it / M, t = it - q * M;
-          const int j = lo * rpt + q;
-          const float out = res[t * ncol + q] + part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t);
-          if (last_layer) h2[(size_t)t * d + j] = out;
-          else st_dev(h2 + (size_t)t * d + j, out);
-        }
-      });
+      epilogue);
 }
 
 // ------------------------------------------------------------------ kernel
