@@ -973,7 +973,7 @@ __device__ __forceinline__ void attn_combine(const KParams& p, Smem sm, int l, i
 // rows reached the cache).
 __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, int l, int seq, int g, int Q,
                                               int p_lo, int p_hi, const Plan& P, float* Qv, float* newk,
-                                              float* newv) {
+                                              float* newv, uint16_t* nkb = nullptr, uint16_t* nvb = nullptr) {
   if (P.U) p_hi = P.F + 1;  // this split also writes the trailing row
   const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
   const int nrows_qkv = (p.H + 2 * p.G) * hd;
@@ -1009,6 +1009,12 @@ __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, 
     newk[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)k1 << 16);
     newv[rr * 128 + i] = __uint_as_float((uint32_t)v0 << 16);
     newv[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)v1 << 16);
+    if (nkb) {
+      nkb[rr * 128 + i] = k0;
+      nkb[rr * 128 + i + hd / 2] = k1;
+      nvb[rr * 128 + i] = v0;
+      nvb[rr * 128 + i + hd / 2] = v1;
+    }
   }
 }
 
@@ -1037,17 +1043,33 @@ __device__ __forceinline__ float sum_groups(float v) {
   return sum_rows(v);     // lane bits 4, 5
 }
 
-// Split-KV GQA decode attention for tasks of at most NQ query vectors
-// (sequence rows * heads per kv head).  Task = (sequence, kv head, split) =
-// this CU; the split's positions are spread over the splits tile by tile.
-// The split streams as K, V tile pairs of 32 positions; wave w takes
-// positions 8w .. 8w+7 of every tile (its 2 KiB quarter, as in a GEMV tile),
-// lane l covering 16 dims (16 * (l & 7)) of position l >> 3, for every query.
-// Scores are kept in log2 units (q is prescaled by log2(e) / sqrt(hd)) so
-// that exp2 applies directly; each wave keeps an online-softmax state per
-// query and rescales its sums only when the running maximum grows by more
-// than 8 (probabilities stay below 2^8).  The four wave states are merged
-// through LDS into the split's partial (maximum stored in natural units).
+// Split-KV GQA decode attention on the matrix cores, for tasks of at most NQ
+// query vectors (sequence rows * heads per kv head).  Task = (sequence, kv
+// head, split) = this CU; the split's positions are spread over the splits
+// tile by tile and stream as K, V tile pairs of 32 positions.  Wave w owns
+// positions 8w .. 8w+7 of every tile (its 2 KiB quarter, as in a GEMV tile)
+// and takes two pairs (a, b) per step: 16 positions r, r < 8 from a.
+//  - Scores S^T[r][q] = K[r][:] . q[:] as 16x16x32 bf16 products with q split
+//    into bf16 high and low parts (two products, fp32 accumulation), so the
+//    scores carry about 16 bits of q and all of K.
+//  - Online softmax on S^T in the product's layout (lane l: query l & 15,
+//    positions 4(l >> 4) .. +3), in log2 units (q is prescaled by log2(e) /
+//    sqrt(hd)); the running maximum is raised only when a score exceeds it
+//    by more than 8, so probabilities stay below 2^8.
+//  - out^T[dim][q] += V^T[dim][r] P^T[r][q] as 16x16x16 bf16 products: V^T
+//    comes from LDS transpose loads, P is split into high and low parts, and
+//    the score layout is already the operand layout P^T needs.
+// The four wave states are merged through LDS into the split's partial
+// (maximum stored in natural units).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const_cast<char*>(p)));
+}
+__device__ __forceinline__ short bf16_bits(__bf16 h) { return __builtin_bit_cast(short, h); }
+
 template <int NQ>
 __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l, Stream& st, const Plan& P,
                                                const Plan& N) {
@@ -1061,17 +1083,21 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   float* newk = Qv + NQ * 128;          // [rps][128]
   float* newv = newk + kMaxRows * 128;  // [rps][128]
   float* wst = newv + kMaxRows * 128;   // [kWaves][NQ][kPartStride] wave states; later combine scratch
+  uint16_t* nkb = reinterpret_cast<uint16_t*>(wst + kWaves * NQ * kPartStride);  // [rps][128] bf16 copies
+  uint16_t* nvb = nkb + kMaxRows * 128;
+  static_assert((NQ * 128 + 2 * kMaxRows * 128 + kWaves * NQ * kPartStride) * 4 + 2 * kMaxRows * 128 * 2 <= kXsBytes,
+                "attention scratch exceeds the x region");
   const int task = blockIdx.x;
   const bool active = task < ntask;
   const int seq = active ? task / (p.G * S) : 0, g = active ? (task / S) % p.G : 0, s = active ? task % S : 0;
   const int p_lo = P.a0, p_hi = P.a1;
-  if (active) attn_prologue(p, ms, l, seq, g, Q, p_lo, p_hi, P, Qv, newk, newv);
+  if (active) attn_prologue(p, ms, l, seq, g, Q, p_lo, p_hi, P, Qv, newk, newv, nkb, nvb);
   __syncthreads();
-  const int d0 = (lane & 7) * 16, pgrp = lane >> 3;
   constexpr float kLog2e = 1.4426950408889634f;
+  const int qq = lane & 15, lg = lane >> 4;
   // Set-up reads are unconditional (every index stays inside its array) and
   // masked by selects: conditional LDS reads would each wait a round trip.
-  // This step's rows inside the split: their positions (uniform), and the span.
+  // This step's rows inside the split's tiles: their positions, and the span.
   int newpos[kMaxRows];
   int new_lo = 1 << 30, new_hi = -1;
 #pragma unroll
@@ -1082,151 +1108,138 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
     new_lo = in ? min(new_lo, pos) : new_lo;
     new_hi = in ? max(new_hi, pos) : new_hi;
   }
-  float qr[NQ][16], acc[NQ][16], m[NQ], lsum[NQ], pq[NQ];
-  int qlim[NQ], qvis[NQ];
+  // q^T operand, lane l: query l & 15, dims 32kb + 8(l >> 4) .. +7, high and low bf16 parts
+  bf16x8_t qh[4], ql[4];
+  const bool qok = active & (qq < Q);
+  {
+    const float* src = Qv + min(qq, NQ - 1) * 128 + lg * 8;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const bool qok = active & (q < Q);
-    const float4* src = reinterpret_cast<const float4*>(Qv + q * 128 + d0);
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 a0 = *reinterpret_cast<const float4*>(src + kb * 32);
+      const float4 a1 = *reinterpret_cast<const float4*>(src + kb * 32 + 4);
+      const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const float4 a = src[e4];
-      qr[q][4 * e4 + 0] = qok ? a.x * kLog2e : 0.f;
-      qr[q][4 * e4 + 1] = qok ? a.y * kLog2e : 0.f;
-      qr[q][4 * e4 + 2] = qok ? a.z * kLog2e : 0.f;
-      qr[q][4 * e4 + 3] = qok ? a.w * kLog2e : 0.f;
+      for (int j = 0; j < 8; ++j) {
+        const float v = qok ? x[j] * kLog2e : 0.f;
+        const __bf16 h = (__bf16)v;
+        qh[kb][j] = h;
+        ql[kb][j] = (__bf16)(v - (float)h);
+      }
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
-    pq[q] = 0.f;
-    m[q] = -INFINITY;
-    lsum[q] = 0.f;
-    const int rowpos = ms->pos[min(seq * rps + q / HG, kMaxRows - 1)];
-    qvis[q] = qok ? rowpos : -1;         // last position the query sees
-    qlim[q] = min(p_hi - 1, qvis[q]);    // ... among the split's tiles
   }
-  // One K row (scores, online-softmax update) and one V row (accumulation)
-  // of the wave's 8 positions; jpos is this lane's position.
-  auto k_row = [&](const float (&f)[16], int jpos, const int (&lim)[NQ]) __attribute__((always_inline)) {
-    // all queries in lockstep (no branch between their chains)
-    float sc[NQ], mt[NQ];
+  const int rowpos = ms->pos[min(seq * rps + qq / HG, kMaxRows - 1)];
+  const int qvis = qok ? rowpos : -1;          // last position the lane's query sees
+  const int qlim = min(p_hi - 1, qvis);        // ... among the split's tiles
+  f32x4_t acc[8];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      float a0 = 0.f, a1 = 0.f;
+  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_l = -INFINITY, lsum = 0.f;
+  // One step over 16 positions: rows r < 8 at kA/vA + r*rs, rows r >= 8 at
+  // kB/vB + (r-8)*rs; position of row r is j0a + r (r < 8) or j0b + r - 8.
+  auto step = [&](const char* kA, const char* kB, const char* vA, const char* vB, int rs, int j0a, int j0b,
+                  int lim) __attribute__((always_inline)) {
+    const int mr = lane & 15;
+    const char* kr = (mr < 8 ? kA : kB) + (mr & 7) * rs + lg * 16;
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        a0 = fmaf(f[e], qr[q][e], a0);
-        a1 = fmaf(f[e + 1], qr[q][e + 1], a1);
-      }
-      sc[q] = (jpos <= lim[q]) ? sum_oct(a0 + a1) : -INFINITY;
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kr + kb * 64));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[kb], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[kb], sc, 0, 0, 0);
     }
-    bool raise = false;
+    float sv[4];
+    bool up = false;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      mt[q] = max_groups(sc[q]);
-      raise |= mt[q] > m[q] + 8.f;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lg + i;
+      const int jpos = r < 8 ? j0a + r : j0b + (r - 8);
+      sv[i] = jpos <= lim ? sc[i] : -INFINITY;
+      up |= sv[i] > m_l + 8.f;
     }
-    if (raise) {  // wave-uniform and rare: raise the reference maxima
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {  // wave-uniform and rare: raise the reference maxima
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool raise = mx > m_l + 8.f;
+      const float corr = !raise ? 1.f : (m_l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_l - mx);
+      lsum *= corr;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const bool up = mt[q] > m[q] + 8.f;
-        const float corr = (!up) ? 1.f : (m[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[q] - mt[q]);
-        lsum[q] *= corr;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[q][e] *= corr;
-        m[q] = up ? mt[q] : m[q];
-      }
+      for (int nb = 0; nb < 8; ++nb) acc[nb] *= corr;
+      m_l = raise ? mx : m_l;
     }
+    s16x4_t ph, pl;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      pq[q] = (sc[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[q] - m[q]);
-      lsum[q] += pq[q];
+    for (int i = 0; i < 4; ++i) {
+      const float pv = sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_l);
+      lsum += pv;
+      const __bf16 h = (__bf16)pv;
+      ph[i] = bf16_bits(h);
+      pl[i] = bf16_bits((__bf16)(pv - (float)h));
+    }
+    // V^T operand by transpose loads: lane 16g + 4j + c reads row 4g + j, dims 16nb + 4c .. +3
+    const int rv = 4 * lg + ((lane >> 2) & 3);
+    const char* vr = (rv < 8 ? vA : vB) + (rv & 7) * rs + (lane & 3) * 8;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const s16x4_t vt = lds_read_tr16(vr + nb * 32);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, acc[nb], 0, 0, 0);
     }
   };
-  auto v_row = [&](const float (&f)[16]) __attribute__((always_inline)) {
+  // This step's rows that fall in a tile of the split replace the tile's
+  // rows in LDS (the tiles may have been loaded before the rows reached the
+  // cache); each wave patches its own quarter after its own wait.
+  auto patch = [&](char* kq, char* vq, int t0q) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[q][e] = fmaf(pq[q], f[e], acc[q][e]);
+    for (int rr = 0; rr < kMaxRows; ++rr) {
+      const int r = newpos[rr] - t0q;
+      if (newpos[rr] >= 0 && r >= 0 && r < 8) {
+        reinterpret_cast<uint32_t*>(kq + r * 256)[lane] = reinterpret_cast<const uint32_t*>(nkb + rr * 128)[lane];
+        reinterpret_cast<uint32_t*>(vq + r * 256)[lane] = reinterpret_cast<const uint32_t*>(nvb + rr * 128)[lane];
+      }
+    }
   };
   st.mark(1);
   settle();
   st.fill(sm, P, N, 0, wave, lane);
-  for (int i = 0; i < P.n; ++i) {
-    st.wait(i);
-    const char* sl = st.slot(sm, i) + wave * 2048 + pgrp * 256 + d0 * 2;
-    const uint4 raw0 = *reinterpret_cast<const uint4*>(sl);
-    const uint4 raw1 = *reinterpret_cast<const uint4*>(sl + 16);
-    const int t0 = p_lo + (i >> 1) * kAttnTile;
-    const bool is_v = (i & 1) != 0;
-    const int jpos = t0 + wave * 8 + pgrp;
-    float f[16];
-    unpack16<uint16_t>(raw0, f);
-    unpack16<uint16_t>(raw1, f + 8);
-    if (new_lo <= t0 + kAttnTile - 1 && new_hi >= t0) {  // a row written this step lies in the tile
-#pragma unroll
-      for (int rr = 0; rr < kMaxRows; ++rr) {  // newpos[rr] is -1 for rr >= rps
-        if (newpos[rr] == jpos) {
-          const float* src = (is_v ? newv : newk) + rr * 128 + d0;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) f[e] = src[e];
-        }
-      }
+  const int nt = P.n / 2;  // position tiles
+  for (int t = 0; t < nt; t += 2) {
+    const bool hb = t + 1 < nt;
+    const int last = hb ? 2 * t + 3 : 2 * t + 1;
+    st.wait(last);
+    char* ka = st.slot(sm, 2 * t) + wave * 2048;
+    char* va = st.slot(sm, 2 * t + 1) + wave * 2048;
+    char* kb = hb ? st.slot(sm, 2 * t + 2) + wave * 2048 : ka;
+    char* vb = hb ? st.slot(sm, 2 * t + 3) + wave * 2048 : va;
+    const int j0a = p_lo + t * kAttnTile + wave * 8;
+    const int j0b = hb ? j0a + kAttnTile : (1 << 30);
+    if (new_lo < p_lo + (t + 2) * kAttnTile && new_hi >= p_lo + t * kAttnTile) {  // rare
+      patch(ka, va, j0a);
+      if (hb) patch(kb, vb, j0b);
     }
-    if (!is_v)
-      k_row(f, jpos, qlim);
-    else
-      v_row(f);
-    st.fill(sm, P, N, i + 1, wave, lane);
+    step(ka, kb, va, vb, 256, j0a, j0b, qlim);
+    st.fill(sm, P, N, last + 1, wave, lane);
   }
-  if (P.U && wave == 0) {  // the trailing row, from its copy in LDS: position group 0 of wave 0
-    float f[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) f[e] = newk[d0 + e];
-    k_row(f, pgrp == 0 ? P.F : (1 << 30), qvis);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) f[e] = newv[d0 + e];
-    v_row(f);
+  if (P.U && wave == 0) {  // the trailing row, from its bf16 copy in LDS (rows r > 0 masked)
+    const char* kr = reinterpret_cast<const char*>(nkb);
+    const char* vr = reinterpret_cast<const char*>(nvb);
+    step(kr, kr, vr, vr, 0, P.F, 1 << 30, qvis);
   }
   st.mark(2);
   if (!active) return;
-  // Wave states.  acc[q][e] is summed over the 8 position groups (lane bits
-  // 3-5) by a reduce-scatter: after halving over bits 5, 4 and 3 a lane
-  // holds, for query 2*b5 + b4, the 8 dims 16*(lane & 7) + 8*b3 + 0..7.
-  // lsum is uniform within a group, so its sum over the groups counts each
-  // position once.
+  // Wave state: lane l holds query l & 15's sums over dims 16nb + 4(l >> 4)
+  // + i; lsum is the lane's share of the query's sum (over 4 lane groups).
   constexpr float kLn2 = 0.6931471805599453f;
-  static_assert(NQ == 4, "the reduce-scatter below is written for 4 queries");
-  {
-    float v[64];
+  float lw = lsum;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+  if (qok) {
+    float* dst = wst + (size_t)(wave * NQ + min(qq, NQ - 1)) * kPartStride;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) v[q * 16 + e] = acc[q][e];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = swap32_sum(v[i], v[32 + i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = swap16_sum(v[i], v[16 + i]);
-    const bool b3 = (lane >> 3) & 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float mine = b3 ? v[8 + i] : v[i];
-      const float other = b3 ? v[i] : v[8 + i];
-      v[i] = mine + dpp<kDppRor8>(other);
-    }
-    const int q = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
-    if (q < Q) {
-      float* dst = wst + (size_t)(wave * NQ + q) * kPartStride + 4 + d0 + 8 * (int)b3;
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const float lw = sum_groups(lsum[q]);
-    if (q < Q && lane == 0) {
-      float* dst = wst + (size_t)(wave * NQ + q) * kPartStride;
-      dst[0] = m[q] == -INFINITY ? -INFINITY : m[q] * kLn2;  // natural units
+    for (int nb = 0; nb < 8; ++nb)
+      *reinterpret_cast<float4*>(dst + 4 + nb * 16 + 4 * lg) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+    if (lg == 0) {
+      dst[0] = m_l == -INFINITY ? -INFINITY : m_l * kLn2;  // natural units
       dst[1] = lw;
     }
   }
