@@ -22,9 +22,9 @@ constexpr int kLdsTotal = 160 * 1024;
 constexpr int kPartBytes = 16 * 1024;
 constexpr int kMiscBytes = 8 * 1024;
 constexpr int kXsBytes = kLdsTotal - kRing * kTileBytes - kPartBytes - kMiscBytes;  // 40 KiB
-constexpr int kPartStride = 132;
+constexpr int kPartStride = 132;        // words per attention partial: m, l, pad, pad, acc[128]
 constexpr int kPartAcc = 3072;          // floats of GEMV partial sums in the part region
-constexpr int kResFloats = kPartBytes / 4 - kPartAcc;  // epilogue residual slice after them        // floats per attention partial: m, l, pad, pad, acc[128]
+constexpr int kResFloats = kPartBytes / 4 - kPartAcc;  // epilogue residual slice after them
 
 // device error flag bits
 enum : unsigned { kErrTimeout = 1u, kErrPosition = 2u, kErrDupPosition = 4u };
@@ -52,7 +52,7 @@ struct DevLayer {
 struct ActLayout {
   size_t h1;      // [M][d]
   size_t qkv;     // [M][(H+2G)*hd]   raw projections (RoPE applied by the reader)
-  size_t part;    // [n_seq][G][S][Q][kPartStride]  attention partials (m, l, -, -, acc[hd])
+  size_t part;    // [n_seq][G][S][Q][kPartStride] 64-bit tag words: attention partials (m, l, -, -, acc[hd])
   size_t o;       // [M][H*hd]
   size_t logits;  // [M][E]
   size_t a_s;     // [M][n_shared][F]  shared SwiGLU activations
@@ -99,7 +99,7 @@ struct KParams {
   char* act;
   ActLayout al;
   unsigned* sync;            // SyncLayout
-  unsigned* attn_cnt;        // [L][n_seq][G]
+  unsigned tag;              // this launch's tag (nonzero; differs from every earlier launch on the handle)
   long long* stamps;         // [n_cu][4*(barriers+1)] or null
   int* t_ids;
   float* t_w;

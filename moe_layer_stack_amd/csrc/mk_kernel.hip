@@ -90,6 +90,21 @@ __device__ __forceinline__ unsigned ld_dev(const unsigned* p) {
 __device__ __forceinline__ void st_dev_u(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 64-bit word = float value (low half) and launch tag (high half), written
+// and read as one single-copy-atomic access, so a reader that sees this
+// launch's tag also sees the value stored with it
+typedef unsigned long long tagword_t;
+__device__ __forceinline__ void st_tag(tagword_t* p, float v, unsigned tag) {
+  __hip_atomic_store(p, ((tagword_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// one tag word by buffer load with cache policy CPOL (a single 8-byte access)
+constexpr int kCpolSc1 = 16;
+constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit buffer descriptor word 3 (gfx9)
+template <int CPOL>
+__device__ __forceinline__ tagword_t ld_word(__amdgpu_buffer_rsrc_t r, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL);
+  return ((tagword_t)v[1] << 32) | v[0];
+}
 
 // 16 bytes per lane, global -> LDS at (wave-uniform base + lane*16),
 // nontemporal.  Issued from inline assembly on purpose: the compiler's
@@ -160,6 +175,7 @@ struct Misc {
   int flag;
   int last;
   int epoch;
+  int gbad[2][kWaves];  // split combine: per wave, words not yet of this launch (by round parity)
   float rinv[kMaxRows];
   float ssq[kWaves * kMaxRows];
   unsigned umask[kMaxExperts];                 // union expert u: rows routed to it
@@ -892,76 +908,98 @@ __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stre
       });
 }
 
-// Online-softmax merge of one partial state (m_z, l_z, acc_z) into (M, L, a).
-__device__ __forceinline__ void softmax_merge(float& M, float& L, float4& a, float mz, float lz, float4 az) {
-  if (mz == -INFINITY) return;
-  const float Mn = fmaxf(M, mz);
-  const float c1 = (M == -INFINITY) ? 0.f : __expf(M - Mn);
-  const float c2 = __expf(mz - Mn);
-  L = L * c1 + lz * c2;
-  a.x = a.x * c1 + az.x * c2; a.y = a.y * c1 + az.y * c2;
-  a.z = a.z * c1 + az.z * c2; a.w = a.w * c1 + az.w * c2;
-  M = Mn;
-}
-
-// The last split of (sequence, kv head g) to finish combines the S split
-// partials of each of its Q query vectors into o.  Partial record (kPartStride
-// floats): m, l, -, -, acc[hd] with acc = sum_t exp(s_t - m) v_t.  Thread =
-// (query, 4 dims, group of splits); each loads its splits' records in
-// batches of 8, merges them, and the split groups are merged through LDS
-// (cst, 6 floats per thread).
-__device__ __forceinline__ void attn_combine(const KParams& p, Smem sm, int l, int seq, int g, int Q, float* cst) {
+// Split combine (flash-decoding reduction): o[q][d] = sum_z w_z acc_z[q][d] /
+// sum_z w_z l_z[q], w_z = exp(m_z[q] - max_z m_z[q]), over the S split
+// partials of (sequence, kv head g).  Partial record: kPartStride tag words,
+// m, l, -, -, acc[hd] (acc = sum_t exp(s_t - m) v_t).  Every split CU takes a
+// slice of the Q*hd outputs, [s*nper, s*nper + nper): it reads, for all
+// splits, the m and l of the slice's queries and the slice's acc values, and
+// reads again until every word carries this launch's tag (no counter, no
+// last arriver).  Thread = (output, group of splits); the groups of an output
+// are neighbouring lanes, merged by butterfly shuffles.
+__device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, int seq, int g, int s, int Q) {
   const int S = p.n_splits, HG = p.H / p.G, rps = p.rps, hd = p.hd;
-  const float* pall = act_f(p, l, p.al.part) + ((size_t)((seq * p.G + g) * S) * Q) * kPartStride;
-  float* o = act_w(p, l, p.al.o);
-  const int QD = Q * (hd / 4);
-  const int ZG = QD >= kThreads ? 1 : kThreads / QD;
-  const int zper = (S + ZG - 1) / ZG;
-  for (int it = threadIdx.x; it < QD * ZG; it += kThreads) {
-    const int qd = it % QD, zg = it / QD;
-    const int q = qd / (hd / 4), d4 = qd % (hd / 4);
-    const int z0 = zg * zper, z1 = min(S, z0 + zper);
-    float M = -INFINITY, L = 0.f;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int zb = z0; zb < z1; zb += 8) {
-      float2 ml[8];
-      float4 av[8];
+  const int nout = Q * hd;
+  const int nper = (nout + S - 1) / S;
+  const int o0 = s * nper, o1 = min(o0 + nper, nout);
+  if (o0 >= o1) return;
+  const int q0 = o0 / hd, nq = (o1 - 1) / hd - q0 + 1;
+  const int nw = 2 * nq + (o1 - o0);  // words per split: (m, l) per query, then the acc slice
+  const int nload = S * nw;
+  const tagword_t* rec0 = reinterpret_cast<const tagword_t*>(act_f(p, l, p.al.part)) +
+                          (size_t)((seq * p.G + g) * S) * Q * kPartStride;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<tagword_t*>(rec0), (short)0, S * Q * kPartStride * 8, kBufferDword3);
+  float* scr = sm.xs;  // [S][nw]
+  Misc* ms = sm.misc;
+  auto word = [&](int it) -> int {  // byte offset of word it
+    const int z = it / nw, w = it - z * nw;
+    const int q = w < 2 * nq ? q0 + (w >> 1) : (o0 + w - 2 * nq) / hd;
+    const int c = w < 2 * nq ? (w & 1) : 4 + (o0 + w - 2 * nq) % hd;
+    return ((z * Q + q) * kPartStride + c) * 8;
+  };
+  if (threadIdx.x == 0) ms->last = 0;  // set on a time-out (read after the first synchronisation)
+  const long long t0 = wall_clock64();
+  const int wave = wave_id();
+  for (int round = 0;; ++round) {
+    int bad = 0;
+    for (int b0 = threadIdx.x; b0 < nload; b0 += 4 * kThreads) {
+      // device-coherent reads (sc1): the writers sit on other XCDs
+      tagword_t v[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (zb + u < z1) {
-          const float* rec = pall + ((size_t)(zb + u) * Q + q) * kPartStride;
-          ml[u] = *reinterpret_cast<const float2*>(rec);
-          av[u] = *reinterpret_cast<const float4*>(rec + 4 + 4 * d4);
+      for (int u = 0; u < 4; ++u) v[u] = ld_word<kCpolSc1>(rsrc, word(min(b0 + u * kThreads, nload - 1)));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int it = b0 + u * kThreads;
+        if (it < nload) {
+          if ((unsigned)(v[u] >> 32) != p.tag) bad = 1;
+          else scr[it] = __uint_as_float((unsigned)v[u]);
         }
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (zb + u < z1) softmax_merge(M, L, a, ml[u].x, ml[u].y, av[u]);
     }
-    if (ZG == 1) {
-      const int row = seq * rps + q / HG, head = g * HG + q % HG;
-      float* dst = o + (size_t)row * (p.H * hd) + head * hd + 4 * d4;
-      const float inv = 1.f / L;
-      st_dev(dst, a.x * inv); st_dev(dst + 1, a.y * inv); st_dev(dst + 2, a.z * inv); st_dev(dst + 3, a.w * inv);
-    } else {
-      float* c = cst + (size_t)it * 6;
-      c[0] = M; c[1] = L; c[2] = a.x; c[3] = a.y; c[4] = a.z; c[5] = a.w;
+    if (threadIdx.x == 0 && wall_clock64() - t0 > p.timeout_ticks) {
+      __hip_atomic_fetch_or(p.sync + SyncLayout::kErr, kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ms->last = 1;
     }
-  }
-  if (ZG > 1) {
+    // workgroup OR of bad through per-wave slots (two sets: a wave that runs
+    // ahead writes the other set, which every wave has read a round ago)
+    const int wbad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+    if ((threadIdx.x & 63) == 0) ms->gbad[round & 1][wave] = wbad;
     __syncthreads();
-    for (int qd = threadIdx.x; qd < QD; qd += kThreads) {
-      float M = -INFINITY, L = 0.f;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int zg = 0; zg < ZG; ++zg) {
-        const float* c = cst + (size_t)(zg * QD + qd) * 6;
-        softmax_merge(M, L, a, c[0], c[1], make_float4(c[2], c[3], c[4], c[5]));
-      }
-      const int q = qd / (hd / 4), d4 = qd % (hd / 4);
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any |= ms->gbad[round & 1][w];
+    if (!any) break;
+    if (ms->last) break;  // timed out: the error flag is set, the values are not used
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __syncthreads();
+  // merge: ZG split groups per output (a power of two, <= 64: one wave)
+  const int nouts = o1 - o0;
+  int ZG = 1;
+  while (ZG * 2 <= 64 && ZG * 2 * nouts <= kThreads) ZG *= 2;
+  float* o = act_w(p, l, p.al.o);
+  for (int t0i = 0; t0i < nouts * ZG; t0i += kThreads) {
+    const int t = t0i + (int)threadIdx.x;
+    const int oi = min(t / ZG, nouts - 1), zg = t % ZG;
+    const int q = (o0 + oi) / hd, d = (o0 + oi) % hd, qi = q - q0;
+    float M = -INFINITY;
+    for (int z = zg; z < S; z += ZG) M = fmaxf(M, scr[z * nw + 2 * qi]);
+    for (int sh = 1; sh < ZG; sh <<= 1) M = fmaxf(M, __shfl_xor(M, sh));
+    float L = 0.f, A = 0.f;
+    for (int z = zg; z < S; z += ZG) {
+      const float mz = scr[z * nw + 2 * qi];
+      const float w = mz == -INFINITY ? 0.f : __expf(mz - M);
+      L = fmaf(w, scr[z * nw + 2 * qi + 1], L);
+      A = fmaf(w, scr[z * nw + 2 * nq + oi], A);
+    }
+    for (int sh = 1; sh < ZG; sh <<= 1) {
+      L += __shfl_xor(L, sh);
+      A += __shfl_xor(A, sh);
+    }
+    if (t < nouts * ZG && zg == 0) {
       const int row = seq * rps + q / HG, head = g * HG + q % HG;
-      float* dst = o + (size_t)row * (p.H * hd) + head * hd + 4 * d4;
-      const float inv = 1.f / L;
-      st_dev(dst, a.x * inv); st_dev(dst + 1, a.y * inv); st_dev(dst + 2, a.z * inv); st_dev(dst + 3, a.w * inv);
+      st_dev(o + (size_t)row * (p.H * hd) + head * hd + d, A / L);
     }
   }
 }
@@ -1245,7 +1283,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   }
   __syncthreads();
   // merge the 4 wave states into the split partial
-  float* part = act_w(p, l, p.al.part) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
+  tagword_t* part = reinterpret_cast<tagword_t*>(act_w(p, l, p.al.part)) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
   for (int it = threadIdx.x; it < Q * (hd / 4 + 1); it += kThreads) {
     const int q = it / (hd / 4 + 1), k4 = it % (hd / 4 + 1);
     float M = -INFINITY;
@@ -1257,13 +1295,13 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
       const float mw = wst[(size_t)(w * NQ + q) * kPartStride];
       cw[w] = (mw == -INFINITY) ? 0.f : __expf(mw - M);
     }
-    float* dst = part + (size_t)q * kPartStride;
+    tagword_t* dst = part + (size_t)q * kPartStride;
     if (k4 == hd / 4) {
       float L = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) L += cw[w] * wst[(size_t)(w * NQ + q) * kPartStride + 1];
-      st_dev(dst + 0, M);
-      st_dev(dst + 1, L);
+      st_tag(dst + 0, M, p.tag);
+      st_tag(dst + 1, L, p.tag);
     } else {
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1271,21 +1309,12 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
         const float* src = wst + (size_t)(w * NQ + q) * kPartStride + 4 + 4 * k4;
         a.x += cw[w] * src[0]; a.y += cw[w] * src[1]; a.z += cw[w] * src[2]; a.w += cw[w] * src[3];
       }
-      st_dev(dst + 4 + 4 * k4, a.x); st_dev(dst + 5 + 4 * k4, a.y);
-      st_dev(dst + 6 + 4 * k4, a.z); st_dev(dst + 7 + 4 * k4, a.w);
+      st_tag(dst + 4 + 4 * k4, a.x, p.tag); st_tag(dst + 5 + 4 * k4, a.y, p.tag);
+      st_tag(dst + 6 + 4 * k4, a.z, p.tag); st_tag(dst + 7 + 4 * k4, a.w, p.tag);
     }
   }
-  wait_all();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* cnt = p.attn_cnt + ((size_t)l * p.n_seq + seq) * p.G + g;
-    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (old + 1u == (unsigned)S);
-    if (last) st_dev_u(cnt, 0u);
-    ms->last = last;
-  }
-  __syncthreads();
-  if (ms->last) attn_combine(p, sm, l, seq, g, Q, wst);
+  __syncthreads();  // the wave states are read before the gather reuses the x region
+  attn_gather(p, sm, l, seq, g, s, Q);
 }
 
 // Split-KV GQA attention.  Task = (sequence, kv head, split) = this CU.
@@ -1443,33 +1472,24 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
   st.mark(2);
   if (!active) return;
   // sum the 4 position groups; lanes 0-15 hold acc for dims d0..d0+7
-  float* part = act_w(p, l, p.al.part) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
+  tagword_t* part = reinterpret_cast<tagword_t*>(act_w(p, l, p.al.part)) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
     const int q = wave + 4 * i;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = sum_rows(acc[i][j]);
     if (q < Q && lane < 16) {
-      float* dst = part + (size_t)q * kPartStride;
+      tagword_t* dst = part + (size_t)q * kPartStride;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) st_dev(dst + 4 + d0 + j, acc[i][j]);
+      for (int j = 0; j < 8; ++j) st_tag(dst + 4 + d0 + j, acc[i][j], p.tag);
       if (lane == 0) {
-        st_dev(dst + 0, m[i]);
-        st_dev(dst + 1, lsum[i]);
+        st_tag(dst + 0, m[i], p.tag);
+        st_tag(dst + 1, lsum[i], p.tag);
       }
     }
   }
-  wait_all();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* cnt = p.attn_cnt + ((size_t)l * p.n_seq + seq) * p.G + g;
-    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (old + 1u == (unsigned)S);
-    if (last) st_dev_u(cnt, 0u);
-    ms->last = last;
-  }
-  __syncthreads();
-  if (ms->last) attn_combine(p, sm, l, seq, g, Q, coef);
+  __syncthreads();  // LDS reads of this task are done before the gather reuses the x region
+  attn_gather(p, sm, l, seq, g, s, Q);
 }
 
 // WO: h1 = h + Wo . o
@@ -2006,6 +2026,10 @@ extern "C" int mk_launch_kernel(const mk::KParams* pp, void* stream) {
   }
   static bool attr_done[5] = {false, false, false, false, false};
   if (!attr_done[idx]) {
+    // the kernel takes all of the CU's LDS dynamically: any static LDS (a
+    // library routine that declares its own) would make the launch fail
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, fn) != hipSuccess || fa.sharedSizeBytes != 0) return -3;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return -1;
     attr_done[idx] = true;
   }

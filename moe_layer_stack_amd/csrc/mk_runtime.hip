@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -56,9 +57,8 @@ struct mk_handle {
   DevLayer* d_layers = nullptr;
   char* d_act = nullptr;
   unsigned* d_sync = nullptr;
-  unsigned* d_attn_cnt = nullptr;
   size_t act_bytes = 0;
-  size_t attn_cnt_bytes = 0;
+  unsigned launch_tag = 0;  // tag of the last launch; the workspace starts zeroed, so 0 is never used
   int32_t* t_ids = nullptr;
   float* t_w = nullptr;
   float* t_logits = nullptr;
@@ -173,6 +173,21 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
     int maxs = (c.kv_capacity + mk::kAttnTile - 1) / mk::kAttnTile;
     if (s > maxs) s = maxs;
     h->n_splits = s;
+    // the split combine gathers, per split, the (m, l) words of the queries
+    // its output slice touches and the slice's acc words into the x region
+    const int Q = c.rows_per_seq * (c.n_heads / c.n_kv_heads);
+    const int nout = Q * hd, nper = (nout + s - 1) / s;
+    int maxw = 0;
+    for (int z = 0; z < s; ++z) {
+      const int o0 = z * nper, o1 = std::min(o0 + nper, nout);
+      if (o0 >= o1) break;
+      maxw = std::max(maxw, 2 * ((o1 - 1) / hd - o0 / hd + 1) + (o1 - o0));
+    }
+    if ((size_t)s * maxw * 4 > (size_t)mk::kXsBytes) {
+      delete h;
+      return fail(MK_ERR_UNSUPPORTED, "attention split combine needs %zu bytes of LDS scratch (%d available)",
+                  (size_t)s * maxw * 4, mk::kXsBytes);
+    }
   }
   {
     // epilogue residual slices (output columns of one CU, every row) live in
@@ -206,7 +221,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   };
   al.h1 = take((size_t)M * d * 4);
   al.qkv = take((size_t)M * (H + 2 * G) * hd * 4);
-  al.part = take((size_t)n_seq * G * h->n_splits * Q * mk::kPartStride * 4);
+  al.part = take((size_t)n_seq * G * h->n_splits * Q * mk::kPartStride * 8);
   al.o = take((size_t)M * H * hd * 4);
   al.logits = take((size_t)M * E * 4);
   al.a_s = take((size_t)M * S * F * 4);
@@ -216,13 +231,11 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   al.stride = align256(off);
   h->al = al;
   h->act_bytes = al.stride * c.n_layers;
-  h->attn_cnt_bytes = c.has_attn ? (size_t)c.n_layers * n_seq * G * 4 : 256;
 
   auto cleanup = [&]() {
     if (h->d_layers) (void)hipFree(h->d_layers);
     if (h->d_act) (void)hipFree(h->d_act);
     if (h->d_sync) (void)hipFree(h->d_sync);
-    if (h->d_attn_cnt) (void)hipFree(h->d_attn_cnt);
     delete h;
   };
   std::vector<DevLayer> hl(c.n_layers);
@@ -233,14 +246,12 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   }
   if (hipMalloc(&h->d_layers, sizeof(DevLayer) * c.n_layers) != hipSuccess ||
       hipMalloc(&h->d_act, h->act_bytes) != hipSuccess ||
-      hipMalloc(&h->d_sync, SyncLayout::kWords * 4) != hipSuccess ||
-      hipMalloc(&h->d_attn_cnt, h->attn_cnt_bytes) != hipSuccess) {
+      hipMalloc(&h->d_sync, SyncLayout::kWords * 4) != hipSuccess) {
     cleanup();
     return fail(MK_ERR_HIP, "workspace allocation failed");
   }
   if (hipMemcpy(h->d_layers, hl.data(), sizeof(DevLayer) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess ||
-      hipMemset(h->d_attn_cnt, 0, h->attn_cnt_bytes) != hipSuccess ||
       hipMemset(h->d_act, 0, h->act_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     cleanup();
     return fail(MK_ERR_HIP, "workspace initialisation failed");
@@ -255,7 +266,6 @@ int mk_destroy(mk_handle* h) {
   if (h->d_layers && hipFree(h->d_layers) != hipSuccess) rc = MK_ERR_HIP;
   if (h->d_act && hipFree(h->d_act) != hipSuccess) rc = MK_ERR_HIP;
   if (h->d_sync && hipFree(h->d_sync) != hipSuccess) rc = MK_ERR_HIP;
-  if (h->d_attn_cnt && hipFree(h->d_attn_cnt) != hipSuccess) rc = MK_ERR_HIP;
   delete h;
   return rc == MK_OK ? MK_OK : fail(rc, "hipFree failed");
 }
@@ -282,7 +292,7 @@ int mk_get_info(const mk_handle* h, mk_info* info) {
   info->barriers_per_step = h->barriers;
   info->attn_splits = h->n_splits;
   info->workspace_bytes =
-      (int64_t)(h->act_bytes + SyncLayout::kWords * 4 + h->attn_cnt_bytes + sizeof(DevLayer) * h->cfg.n_layers);
+      (int64_t)(h->act_bytes + SyncLayout::kWords * 4 + sizeof(DevLayer) * h->cfg.n_layers);
   return MK_OK;
 }
 
@@ -335,11 +345,13 @@ int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* position
     p.act = h->d_act;
     p.al = h->al;
     p.sync = h->d_sync;
-    p.attn_cnt = h->d_attn_cnt;
+    if (++h->launch_tag == 0) h->launch_tag = 1;
+    p.tag = h->launch_tag;
     p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
     p.stamps = reinterpret_cast<long long*>(h->stamps);
     int e = mk_launch_kernel(&p, stream);
     if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
+    if (e == -3) return fail(MK_ERR_HIP, "the kernel declares static LDS, which leaves no room for its ring");
     if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));
   }
   return MK_OK;
@@ -354,8 +366,7 @@ int mk_sync(mk_handle* h, void* stream) {
   if (e != hipSuccess) return fail(MK_ERR_HIP, "reading the device error flag failed: %s", hipGetErrorString(e));
   if (err == 0) return MK_OK;
   // reset barrier state and counters so the handle can run again
-  if (hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess ||
-      hipMemset(h->d_attn_cnt, 0, h->attn_cnt_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+  if (hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
     return fail(MK_ERR_HIP, "resetting the barrier state failed");
   if (err & mk::kErrTimeout) return fail(MK_ERR_TIMEOUT, "a grid barrier timed out (device flag 0x%x)", err);
   return fail(MK_ERR_INVALID_ARG, "a position was outside the cache or repeated within a sequence (flag 0x%x)", err);
