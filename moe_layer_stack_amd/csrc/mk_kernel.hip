@@ -676,6 +676,16 @@ __device__ __forceinline__ void load_x_norm(XRegs<WT, MT>& xr, Smem sm, const fl
   }
 }
 
+// Part-block slots per wave: a wave reads 2 KiB of every tile as two 1 KiB
+// chunks; with bf16 weights every row is at least 2 KiB (the host checks), so
+// both chunks of a wave lie in one row and their sums are added before the
+// cross-lane reduction (one slot); fp32 rows may be 1 KiB (two slots).
+template <typename WT>
+struct Slots {
+  static constexpr int C = sizeof(WT) == 2 ? 1 : 2;
+  static constexpr int kUnitLog2 = C == 1 ? 11 : 10;  // bytes of tile behind one slot
+};
+
 // Tiles consumed per step of the GEMV loop: one cross-lane reduction serves
 // the whole group (2 * G * MT values per lane).
 template <int MT>
@@ -694,7 +704,8 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
                                            int lane) {
   constexpr int G = GroupOf<MT>::G;
   constexpr int EPL = XRegs<WT, MT>::EPL;
-  constexpr int NV = G * 2 * MT;
+  constexpr int C = Slots<WT>::C;
+  constexpr int NV = G * C * MT;
   uint4 wv[G][2];
   const int rs0 = (st.slot0 + i) % kRing;
 #pragma unroll
@@ -707,6 +718,8 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
     }
   }
   float acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = 0.f;
 #pragma unroll
   for (int u = 0; u < G; ++u) {
 #pragma unroll
@@ -723,16 +736,16 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
             s1 = fmaf(w[j + 1], xr.v[t][c][j + 1], s1);
           }
         }
-        acc[(u * 2 + c) * MT + t] = (s0 + s1) * tw[t];
+        acc[(u * C + (C == 1 ? 0 : c)) * MT + t] += (s0 + s1) * tw[t];
       }
     }
   }
   const float r = xreduce<NV>(acc, lane);
   if (xreduce_writer<NV>(lane)) {
     const int idx = xreduce_index<NV>(lane);
-    const int u = idx / (2 * MT), c = (idx / MT) & 1, t = idx % MT;
+    const int u = idx / (C * MT), c = (idx / MT) % C, t = idx % MT;
     if (u < g) {
-      float* dst = sm.part + (size_t)(blk0 + u) * (kWaves * 2 * MT) + (wave * 2 + c) * MT + t;
+      float* dst = sm.part + (size_t)(blk0 + u) * (kWaves * C * MT) + (wave * C + c) * MT + t;
       if (accum) *dst += r;
       else *dst = r;
     }
@@ -740,11 +753,12 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
 }
 
 // One row per step: this wave's quarter of the g <= G tiles i .. i+g-1
-// against x, each chunk's dot product scaled by tw and added to the lane's
-// running sums pacc[u*2 + c] (no cross-lane reduction here).
+// against x, each slot's dot product scaled by tw and added to the lane's
+// running sums pacc[u*C + c] (no cross-lane reduction here).
 template <typename WT>
 __device__ __forceinline__ void gemv_acc1(Smem sm, const Stream& st, int i, int g, const XRegs<WT, 1>& xr, float tw,
-                                          float (&pacc)[GroupOf<1>::G * 2], int wave, int lane) {
+                                          float (&pacc)[GroupOf<1>::G * Slots<WT>::C], int wave, int lane) {
+  constexpr int C = Slots<WT>::C;
   constexpr int G = GroupOf<1>::G;
   constexpr int EPL = XRegs<WT, 1>::EPL;
   uint4 wv[G][2];
@@ -770,7 +784,7 @@ __device__ __forceinline__ void gemv_acc1(Smem sm, const Stream& st, int i, int 
         s0 = fmaf(w[j], xr.v[0][c][j], s0);
         s1 = fmaf(w[j + 1], xr.v[0][c][j + 1], s1);
       }
-      if (u < g) pacc[u * 2 + c] = fmaf(s0 + s1, tw, pacc[u * 2 + c]);
+      if (u < g) pacc[u * C + (C == 1 ? 0 : c)] = fmaf(s0 + s1, tw, pacc[u * C + (C == 1 ? 0 : c)]);
     }
   }
 }
@@ -794,24 +808,28 @@ __device__ __forceinline__ void seg_all(Seg<MT>& sg, int M) {
   for (int t = 0; t < MT; ++t) sg.tw[t] = 1.f;
 }
 
-// part block layout: [wave][c][MT]; the row of (wave, c) in a tile of
-// 2^lrb-byte rows is (wave*2048 + c*1024) >> lrb.
-template <int MT>
+// part block layout: [wave][c][MT] with C slots c per wave; slot (wave, c)
+// holds the tile bytes from wave*2048 + c*2^U (U = kUnitLog2), so row q of
+// 2^lrb-byte rows covers slots q*upr .. q*upr+upr-1, upr = 2^(lrb-U).
+template <typename WT, int MT>
 __device__ __forceinline__ float part_row(const float* part, int block, int q, int lrb, int t) {
-  // row q of 2^lrb-byte rows (>= 1 KiB) covers chunks q*cpr .. q*cpr+cpr-1;
-  // all 8 chunks are read (no branches between the LDS reads) and masked
-  const float* b = part + (size_t)block * (kWaves * 2 * MT);
-  const int cpr = 1 << (lrb - 10), c0 = q * cpr;
-  float v[kWaves * 2];
+  constexpr int C = Slots<WT>::C;
+  constexpr int NS = kWaves * C;
+  const float* b = part + (size_t)block * (NS * MT);
+  const int upr = 1 << (lrb - Slots<WT>::kUnitLog2), c0 = q * upr;
+  float v[NS];
 #pragma unroll
-  for (int ch = 0; ch < kWaves * 2; ++ch) v[ch] = b[ch * MT + t];
-  // One use of all eight values before the selects: otherwise the compiler
-  // moves each read under its select's branch and the reads run one after
-  // another, a full LDS round trip each.
-  asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+  for (int ch = 0; ch < NS; ++ch) v[ch] = b[ch * MT + t];
+  // One use of every value before the selects: otherwise the compiler moves
+  // each read under its select's branch and the reads run one after another,
+  // a full LDS round trip each.
+  if constexpr (NS == 8)
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+  else
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
   float s = 0.f;
 #pragma unroll
-  for (int ch = 0; ch < kWaves * 2; ++ch) s += (ch >= c0 && ch < c0 + cpr) ? v[ch] : 0.f;
+  for (int ch = 0; ch < NS; ++ch) s += (ch >= c0 && ch < c0 + upr) ? v[ch] : 0.f;
   return s;
 }
 
@@ -893,7 +911,7 @@ __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stre
                       P.lrb);
   zero_part(sm);
   __syncthreads();
-  constexpr int kRound = kPartAcc / (kWaves * 2 * MT);
+  constexpr int kRound = kPartAcc / (kWaves * Slots<WT>::C * MT);
   const Misc* ms = sm.misc;
   const int rpt = P.rpt, lo = P.lo, lrb = P.lrb, n = P.n;
   run_gemv<WT, MT>(
@@ -903,7 +921,7 @@ __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stre
         for (int it = threadIdx.x; it < nr * M; it += kThreads) {
           const int q = it / M, t = it - q * M;
           const int row = (lo + first) * rpt + q;
-          st_dev(qkv + (size_t)t * nrows + row, part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t) * ms->rinv[t]);
+          st_dev(qkv + (size_t)t * nrows + row, part_row<WT, MT>(sm.part, q / rpt, q % rpt, lrb, t) * ms->rinv[t]);
         }
       });
 }
@@ -1508,7 +1526,7 @@ __device__ __forceinline__ void phase_wo(const KParams& p, Smem sm, int l, Strea
   const int ncol = n * rpt;
   load_res(sm, h, nullptr, d, lo * rpt, ncol, M);
   __syncthreads();
-  constexpr int kRound = kPartAcc / (kWaves * 2 * MT);
+  constexpr int kRound = kPartAcc / (kWaves * Slots<WT>::C * MT);
   const float* res = res_slice(sm);
   run_gemv<WT, MT>(
       sm, st, P, N, xr, [&](int i, Seg<MT>& sg) { seg_rounds<MT>(sg, i, 0, n, kRound, M); },
@@ -1517,7 +1535,7 @@ __device__ __forceinline__ void phase_wo(const KParams& p, Smem sm, int l, Strea
         for (int it = threadIdx.x; it < nr * M; it += kThreads) {
           const int q = it / M, t = it - q * M;
           const int row = (lo + first) * rpt + q;
-          st_dev(h1 + (size_t)t * d + row, res[t * ncol + row - lo * rpt] + part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t));
+          st_dev(h1 + (size_t)t * d + row, res[t * ncol + row - lo * rpt] + part_row<WT, MT>(sm.part, q / rpt, q % rpt, lrb, t));
         }
       });
 }
@@ -1540,7 +1558,7 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
   if (has_bias) load_res(sm, br, nullptr, 0, 0, E, 1);
   __syncthreads();
   const float* res = res_slice(sm);
-  constexpr int kRound = (kPartAcc / (kWaves * 2 * MT)) & ~1;  // even: a pair stays in one round
+  constexpr int kRound = (kPartAcc / (kWaves * Slots<WT>::C * MT)) & ~1;  // even: a pair stays in one round
   const Misc* ms = sm.misc;
   const int rpt = P.rpt, lrb = P.lrb, n1 = P.n1, n = P.n, r_lo = P.lo, p_lo = P.lo2, fb_per = P.fb_per;
   run_gemv<WT, MT>(
@@ -1556,7 +1574,7 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
             const int q = it / M, t = it - q * M;
             const int e = (r_lo + first) * rpt + q;
             if (e >= E) continue;
-            float v = part_row<MT>(sm.part, q / rpt, q % rpt, lrb, t) * ms->rinv[t];
+            float v = part_row<WT, MT>(sm.part, q / rpt, q % rpt, lrb, t) * ms->rinv[t];
             if (has_bias) v += res[e];
             st_dev(logits + (size_t)t * E + e, v);
           }
@@ -1568,8 +1586,8 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
             const int pj = p_lo + k0 / 2 + pr;
             const int sx = pj / fb_per, f = (pj % fb_per) * rpt + q;
             const float ri = ms->rinv[t];
-            const float gv = part_row<MT>(sm.part, 2 * pr, q, lrb, t) * ri;
-            const float uv = part_row<MT>(sm.part, 2 * pr + 1, q, lrb, t) * ri;
+            const float gv = part_row<WT, MT>(sm.part, 2 * pr, q, lrb, t) * ri;
+            const float uv = part_row<WT, MT>(sm.part, 2 * pr + 1, q, lrb, t) * ri;
             st_dev(a_s + ((size_t)t * S + sx) * F + f, gv / (1.f + __expf(-gv)) * uv);
           }
         }
@@ -1719,7 +1737,7 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
   wait_all();
   __syncthreads();
   const Misc* ms = sm.misc;
-  constexpr int kRound = (kPartAcc / (kWaves * 2 * MT)) & ~1;  // even: a gate/up pair stays in one round
+  constexpr int kRound = (kPartAcc / (kWaves * Slots<WT>::C * MT)) & ~1;  // even: a gate/up pair stays in one round
   const int n1 = P.n1, n = P.n, nj = P.nj, lrb = P.lrb, lrb2 = P.lrb2, rpt = P.rpt, rpt2 = P.rpt2;
   const int fb_per = P.fb_per, sd_lo = P.lo, p_lo = P.lo2;
   XRegs<WT, MT> xw;  // a_s rows for the shared-down tiles, then y
@@ -1758,7 +1776,7 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
           for (int it = threadIdx.x; it < nj * rpt * M; it += kThreads) {
             const int u = it / (rpt * M), q = (it / M) % rpt, t = it % M;
             const int j = (sd_lo + u) * rpt + q;
-            st_dev(ys + (size_t)t * d + j, part_row<MT>(sm.part, u, q, lrb, t));
+            st_dev(ys + (size_t)t * d + j, part_row<WT, MT>(sm.part, u, q, lrb, t));
           }
         } else {
           const int k0 = first - n1;
@@ -1770,8 +1788,8 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
             const int sl = ms->uslot[u * kMaxRows + t];
             if (sl < 0) continue;
             const float ri = ms->rinv[t];
-            const float gv = part_row<MT>(sm.part, 2 * pr, q, lrb2, t) * ri;
-            const float uv = part_row<MT>(sm.part, 2 * pr + 1, q, lrb2, t) * ri;
+            const float gv = part_row<WT, MT>(sm.part, 2 * pr, q, lrb2, t) * ri;
+            const float uv = part_row<WT, MT>(sm.part, 2 * pr + 1, q, lrb2, t) * ri;
             st_dev(a + ((size_t)t * k + sl) * F + f, gv / (1.f + __expf(-gv)) * uv);
           }
         }
@@ -1806,7 +1824,7 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
     for (int it = threadIdx.x; it < ncol * M; it += kThreads) {
       const int q = MT == 1 ? it : it / M, t = MT == 1 ? 0 : it - q * M;
       const int j = lo * rpt + q;
-      const float out = res[t * ncol + q] + part_row<MT>(sm.part, q >> (13 - lrb), q & (rpt - 1), lrb, t);
+      const float out = res[t * ncol + q] + part_row<WT, MT>(sm.part, q >> (13 - lrb), q & (rpt - 1), lrb, t);
       if (last_layer) h2[(size_t)t * d + j] = out;
       else st_dev(h2 + (size_t)t * d + j, out);
     }
@@ -1829,9 +1847,10 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
         const int ro[1] = {__builtin_amdgcn_readlane(xoff_l, u)};
         load_x_lds<WT, 1>(x, sm.xs, ro, 1u, wave, lane, lrb);
       };
-      float pacc[G * 2];
+      constexpr int C = Slots<WT>::C;
+      float pacc[G * C];
 #pragma unroll
-      for (int v = 0; v < G * 2; ++v) pacc[v] = 0.f;
+      for (int v = 0; v < G * C; ++v) pacc[v] = 0.f;
       st.mark(1);
       settle();
       st.fill(sm, P, N, 0, wave, lane);
@@ -1845,10 +1864,10 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
         st.fill(sm, P, N, j + nj, wave, lane);
         xa = xb;
       }
-      const float r = xreduce<G * 2>(pacc, lane);
-      if (xreduce_writer<G * 2>(lane)) {
-        const int idx = xreduce_index<G * 2>(lane);
-        if (idx / 2 < nj) sm.part[(idx / 2) * (kWaves * 2) + wave * 2 + (idx & 1)] = r;
+      const float r = xreduce<G * C>(pacc, lane);
+      if (xreduce_writer<G * C>(lane)) {
+        const int idx = xreduce_index<G * C>(lane);
+        if (idx / C < nj) sm.part[(idx / C) * (kWaves * C) + wave * C + idx % C] = r;
       }
       __syncthreads();
       epilogue(0, n - 1);

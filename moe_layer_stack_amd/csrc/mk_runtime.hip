@@ -76,6 +76,11 @@ int validate(const mk_config* c) {
     return fail(MK_ERR_UNSUPPORTED, "d_model rows must be 1, 2, 4 or 8 KiB (d=%d)", c->d_model);
   if (c->d_ff < 1 || !is_row_size_ok((long long)c->d_ff * es))
     return fail(MK_ERR_UNSUPPORTED, "d_ff rows must be 1, 2, 4 or 8 KiB (F=%d)", c->d_ff);
+  // bf16 GEMV tiles merge the two 1 KiB chunks a wave reads before the
+  // cross-lane reduction, which needs rows of at least 2 KiB
+  if (c->dtype == MK_BF16 && (c->d_model * es < 2048 || c->d_ff * es < 2048 ||
+                              (c->has_attn && (long long)c->n_heads * c->head_dim * es < 2048)))
+    return fail(MK_ERR_UNSUPPORTED, "bf16 rows (d_model, d_ff, n_heads*head_dim) must be at least 2 KiB");
   const int rpt_d = 8192 / (c->d_model * es);
   if (c->d_ff % rpt_d) return fail(MK_ERR_UNSUPPORTED, "d_ff must be a multiple of %d", rpt_d);
   const int rpt_f = 8192 / (c->d_ff * es);

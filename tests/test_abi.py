@@ -85,6 +85,8 @@ def _layers(n):
     (dict(rows=4, rows_per_seq=3), -1),
     (dict(has_attn=1, n_heads=3, n_kv_heads=2, head_dim=128, d_model=256, kv_capacity=16), -1),
     (dict(has_attn=1, n_heads=2, n_kv_heads=1, head_dim=64, kv_capacity=16), -2),
+    (dict(dtype=1, d_model=512, d_ff=1024), -2),   # bf16 rows below 2 KiB
+    (dict(dtype=1, d_model=1024, d_ff=512), -2),
 ])
 def test_create_rejects_bad_config(mk, kw, status):
     with pytest.raises(mk.MkError) as ei:
