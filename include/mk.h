@@ -50,7 +50,8 @@
  * Errors.  Every call returns MK_OK (0) or a negative mk_status.  Argument
  * checks that need no device data happen at once.  Conditions only the
  * device can see (a position outside [0, capacity), two rows of one
- * sequence at the same position, a grid barrier that does not complete) set
+ * sequence at the same position, a grid barrier or an attention split
+ * combine that does not complete within the device watchdog) set
  * a device error flag; the step then skips the affected writes and ends, and
  * the next mk_sync returns the error and clears it.  mk_strerror describes a
  * status; mk_last_error describes the most recent failure of this thread.
@@ -76,7 +77,7 @@ typedef enum mk_status {
   MK_ERR_UNSUPPORTED = -2, /* shape or dtype outside what the kernels implement */
   MK_ERR_DEVICE = -3,      /* no suitable gfx950 device, or one workgroup per CU cannot be co-resident */
   MK_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
-  MK_ERR_TIMEOUT = -5      /* a grid barrier did not complete (device watchdog) */
+  MK_ERR_TIMEOUT = -5      /* a grid barrier or split combine did not complete (device watchdog) */
 } mk_status;
 
 typedef enum mk_dtype { MK_F32 = 0, MK_BF16 = 1 } mk_dtype;
