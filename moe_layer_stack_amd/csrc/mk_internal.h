@@ -12,6 +12,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = 8192;        // weight tile streamed through the LDS ring
 constexpr int kChunk = 1024;            // one global_load_lds: 64 lanes x 16 B
 constexpr int kRing = 12;               // ring slots (tiles in flight per CU)
+constexpr int kSlotBytes = kTileBytes + 128;  // slot pitch: four neighbouring slots start in different LDS bank halves
 constexpr int kMaxRows = 8;             // M
 constexpr int kMaxExperts = 64;         // E (one lane per expert in top-k)
 constexpr int kMaxTopK = 8;
@@ -21,7 +22,7 @@ constexpr int kAttnTile = 32;           // positions per KV tile (hd = 128 bf16 
 constexpr int kLdsTotal = 160 * 1024;
 constexpr int kPartBytes = 16 * 1024;
 constexpr int kMiscBytes = 8 * 1024;
-constexpr int kXsBytes = kLdsTotal - kRing * kTileBytes - kPartBytes - kMiscBytes;  // 40 KiB
+constexpr int kXsBytes = kLdsTotal - kRing * kSlotBytes - kPartBytes - kMiscBytes;  // 38.5 KiB
 constexpr int kPartStride = 132;        // words per attention partial: m, l, pad, pad, acc[128]
 constexpr int kPartAcc = 3072;          // floats of GEMV partial sums in the part region
 constexpr int kResFloats = kPartBytes / 4 - kPartAcc;  // epilogue residual slice after them

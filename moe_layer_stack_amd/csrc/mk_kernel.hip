@@ -545,7 +545,7 @@ struct Stream {
     if (ts && threadIdx.x == 0) ts[k] = wall_clock64();
   }
   __device__ __forceinline__ char* slot(Smem sm, int j) const {
-    return sm.ring + (size_t)((slot0 + j) % kRing) * kTileBytes;
+    return sm.ring + (size_t)((slot0 + j) % kRing) * kSlotBytes;
   }
   // issue while ring slots are free; `consumed` tiles of cur are done
   __device__ __forceinline__ void fill(Smem sm, const Plan& cur, const Plan& nxt, int consumed, int wave,
@@ -554,7 +554,7 @@ struct Stream {
     // consumed (their values fed the arithmetic), so no LDS wait is needed.
     const int limit = min(consumed + kRing, cur.n + nxt.n);
     for (; issued < limit; ++issued) {
-      const unsigned s = ring_lds + (unsigned)islot * kTileBytes;
+      const unsigned s = ring_lds + (unsigned)islot * kSlotBytes;
       islot = islot == kRing - 1 ? 0 : islot + 1;
       if (issued < cur.n) {
         if ((unsigned)(issued - wc.w0) >= 64u) wc = build_win(cur, issued, sm.misc, lane);
@@ -588,12 +588,36 @@ __device__ __forceinline__ int lane_k0(int wave, int lane, int c, int lrb) {
   return (off & ((1 << lrb) - 1)) / (int)sizeof(WT);
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 // x registers: the EPL activation elements each chunk of this lane meets, per token
 template <typename WT, int MT>
 struct XRegs {
   static constexpr int EPL = 16 / sizeof(WT);
   float v[MT][2][EPL];
 };
+// 8 rows, bf16 weights: x for the matrix-core GEMV (gemv_group below).  Lane
+// 4b + t holds tokens t and t + 4 (index h) at the k-elements kq + kc*64 + 4b
+// + j (kc < 16, j < 4; kq = the wave's first k-element of its 2 KiB quarter of
+// a tile), as bf16 high and low parts of the fp32 value.
+template <>
+struct XRegs<uint16_t, 8> {
+  static constexpr int EPL = 8;
+  s16x4_t hi[2][16];
+  s16x4_t lo[2][16];
+};
+__device__ __forceinline__ void split_bf16x4(float4 a, s16x4_t& hi, s16x4_t& lo) {
+  const float x[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 h = (__bf16)x[j];
+    hi[j] = __builtin_bit_cast(short, h);
+    lo[j] = __builtin_bit_cast(short, (__bf16)(x[j] - (float)h));
+  }
+}
+__device__ __forceinline__ int m8_kq(int wave, int lrb) { return ((wave * 2048) & ((1 << lrb) - 1)) >> 1; }
 
 // Fill x registers from fp32 rows: token t reads src + t*ld (+ k0); gam
 // (nullable) multiplies element-wise.  Tokens >= M are zero.
@@ -676,6 +700,78 @@ __device__ __forceinline__ void load_x_norm(XRegs<WT, MT>& xr, Smem sm, const fl
   }
 }
 
+// x loaders for 8 rows with bf16 weights (the matrix-core layout of
+// XRegs<uint16_t, 8>): token t4 + 4h, elements kq + kc*64 + 4b + j.
+template <>
+__device__ __forceinline__ void load_x<uint16_t, 8>(XRegs<uint16_t, 8>& xr, const float* src, int ld,
+                                                    const uint16_t* gam, int M, int wave, int lane, int lrb) {
+  const int t4 = lane & 3, b = lane >> 2;
+  const int k0 = m8_kq(wave, lrb) + b * 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = t4 + 4 * h;
+    const bool ok = t < M;
+    const float* s = src + (size_t)(ok ? t : 0) * ld + k0;
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc) {
+      float4 a = *reinterpret_cast<const float4*>(s + kc * 64);
+      if (gam) {
+        const uint2 gg = *reinterpret_cast<const uint2*>(gam + k0 + kc * 64);
+        a.x *= __uint_as_float(gg.x << 16); a.y *= __uint_as_float(gg.x & 0xffff0000u);
+        a.z *= __uint_as_float(gg.y << 16); a.w *= __uint_as_float(gg.y & 0xffff0000u);
+      }
+      if (!ok) a = make_float4(0.f, 0.f, 0.f, 0.f);
+      split_bf16x4(a, xr.hi[h][kc], xr.lo[h][kc]);
+    }
+  }
+}
+template <>
+__device__ __forceinline__ void load_x_norm<uint16_t, 8>(XRegs<uint16_t, 8>& xr, Smem sm, const float* src, int ld,
+                                                         const uint16_t* gam, int M, int d, float eps, int wave,
+                                                         int lane, int lrb) {
+  const int t4 = lane & 3, b = lane >> 2;
+  const int k0 = m8_kq(wave, lrb) + b * 4;
+  float ss[2] = {0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = t4 + 4 * h;
+    const bool ok = t < M;
+    const float* s = src + (size_t)(ok ? t : 0) * ld + k0;
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc) {
+      float4 a = *reinterpret_cast<const float4*>(s + kc * 64);
+      if (!ok) a = make_float4(0.f, 0.f, 0.f, 0.f);
+      ss[h] = fmaf(a.x, a.x, fmaf(a.y, a.y, fmaf(a.z, a.z, fmaf(a.w, a.w, ss[h]))));
+      const uint2 gg = *reinterpret_cast<const uint2*>(gam + k0 + kc * 64);
+      a.x *= __uint_as_float(gg.x << 16); a.y *= __uint_as_float(gg.x & 0xffff0000u);
+      a.z *= __uint_as_float(gg.y << 16); a.w *= __uint_as_float(gg.y & 0xffff0000u);
+      split_bf16x4(a, xr.hi[h][kc], xr.lo[h][kc]);
+    }
+  }
+  // sum of squares of token t over the workgroup: the lanes of one t (bits
+  // 2-5) here, the waves through LDS; each element is met by rpt waves
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float x = ss[h];
+    x += dpp<kDppRor4>(x);
+    x += dpp<kDppRor8>(x);
+    ss[h] = sum_rows(x);
+  }
+  if (b == 0) {
+    sm.misc->ssq[wave * kMaxRows + t4] = ss[0];
+    sm.misc->ssq[wave * kMaxRows + t4 + 4] = ss[1];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < M) {
+    const int t = threadIdx.x;
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += sm.misc->ssq[w * kMaxRows + t];
+    const float rpt = (float)(kTileBytes >> lrb);
+    sm.misc->rinv[t] = 1.0f / sqrtf(tot / (rpt * (float)d) + eps);
+  }
+}
+
 // Part-block slots per wave: a wave reads 2 KiB of every tile as two 1 KiB
 // chunks; with bf16 weights every row is at least 2 KiB (the host checks), so
 // both chunks of a wave lie in one row and their sums are added before the
@@ -687,10 +783,11 @@ struct Slots {
 };
 
 // Tiles consumed per step of the GEMV loop: one cross-lane reduction serves
-// the whole group (2 * G * MT values per lane).
-template <int MT>
+// the whole group.  8 rows with bf16 weights: groups of 4 tiles (the matrix
+// cores take 4 weight rows at a time).
+template <typename WT, int MT>
 struct GroupOf {
-  static constexpr int G = MT == 1 ? 4 : 1;
+  static constexpr int G = (MT == 1 || sizeof(WT) == 2) ? 4 : 1;
 };
 
 // This wave's quarter of g <= G consecutive tiles (ring slots of tiles i ..
@@ -702,7 +799,7 @@ template <typename WT, int MT>
 __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int g, const XRegs<WT, MT>& xr,
                                            unsigned tmask, const float (&tw)[MT], int blk0, bool accum, int wave,
                                            int lane) {
-  constexpr int G = GroupOf<MT>::G;
+  constexpr int G = GroupOf<WT, MT>::G;
   constexpr int EPL = XRegs<WT, MT>::EPL;
   constexpr int C = Slots<WT>::C;
   constexpr int NV = G * C * MT;
@@ -712,7 +809,7 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
   for (int u = 0; u < G; ++u) {
     if (u < g) {
       const int rs = rs0 + u < kRing ? rs0 + u : rs0 + u - kRing;
-      const char* sl = sm.ring + (size_t)rs * kTileBytes + wave * 2048 + lane * 16;
+      const char* sl = sm.ring + (size_t)rs * kSlotBytes + wave * 2048 + lane * 16;
       wv[u][0] = *reinterpret_cast<const uint4*>(sl);
       wv[u][1] = *reinterpret_cast<const uint4*>(sl + 1024);
     }
@@ -752,14 +849,68 @@ __device__ __forceinline__ void gemv_group(Smem sm, const Stream& st, int i, int
   }
 }
 
+// 8 rows, bf16 weights, on the matrix cores.  A group is 4 tiles; for a wave
+// each holds the 1024 k-elements of its 2 KiB quarter of one weight row r.
+// v_mfma_f32_4x4x4_16b_bf16 computes 16 independent 4x4x4 blocks: block b
+// takes the k-elements kc*64 + 4b .. +3 of 4 tokens (A: lane 4b + t) and of
+// 4 rows (B: lane 4b + r), so one instruction covers 64 k-elements of
+// 4 tokens x 4 rows and 16 of them the quarter.  x enters as bf16 high and
+// low parts (two products, fp32 accumulation); the weights are bf16 exactly.
+// D_b[t][r] (lane 4b + r, register t) is summed over the 16 blocks by row
+// rotations and the permlane swaps, then over the waves through the part
+// block, as on the vector path.  Slot pitch kSlotBytes keeps the 4 rows of
+// one read in different LDS bank halves.
+template <>
+__device__ __forceinline__ void gemv_group<uint16_t, 8>(Smem sm, const Stream& st, int i, int g,
+                                                        const XRegs<uint16_t, 8>& xr, unsigned tmask,
+                                                        const float (&tw)[8], int blk0, bool accum, int wave,
+                                                        int lane) {
+  const int r = lane & 3, b = lane >> 2;
+  const int rs0 = (st.slot0 + i) % kRing;
+  const int u = r < g ? r : 0;  // rows past the group read row 0; their sums are dropped
+  const int rs = rs0 + u < kRing ? rs0 + u : rs0 + u - kRing;
+  const char* wp = sm.ring + (size_t)rs * kSlotBytes + wave * 2048 + b * 8;
+  f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < 16; ++kc) {
+    const s16x4_t w = *reinterpret_cast<const s16x4_t*>(wp + kc * 128);
+    d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.hi[0][kc], w, d0, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.lo[0][kc], w, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.hi[1][kc], w, d1, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.lo[1][kc], w, d1, 0, 0, 0);
+  }
+  float v[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[t] = d0[t];
+    v[t + 4] = d1[t];
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {  // over the 16 blocks: lane bits 2, 3 (rotations), 4, 5 (swaps)
+    float x = v[t];
+    x += dpp<kDppRor4>(x);
+    x += dpp<kDppRor8>(x);
+    v[t] = sum_rows(x);
+  }
+  if (b == 0 && r < g) {
+    float* dst = sm.part + (size_t)(blk0 + r) * (kWaves * 8) + wave * 8;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float val = ((tmask >> t) & 1u) ? v[t] * tw[t] : 0.f;
+      if (accum) dst[t] += val;
+      else dst[t] = val;
+    }
+  }
+}
+
 // One row per step: this wave's quarter of the g <= G tiles i .. i+g-1
 // against x, each slot's dot product scaled by tw and added to the lane's
 // running sums pacc[u*C + c] (no cross-lane reduction here).
 template <typename WT>
 __device__ __forceinline__ void gemv_acc1(Smem sm, const Stream& st, int i, int g, const XRegs<WT, 1>& xr, float tw,
-                                          float (&pacc)[GroupOf<1>::G * Slots<WT>::C], int wave, int lane) {
+                                          float (&pacc)[GroupOf<WT, 1>::G * Slots<WT>::C], int wave, int lane) {
   constexpr int C = Slots<WT>::C;
-  constexpr int G = GroupOf<1>::G;
+  constexpr int G = GroupOf<WT, 1>::G;
   constexpr int EPL = XRegs<WT, 1>::EPL;
   uint4 wv[G][2];
   const int rs0 = (st.slot0 + i) % kRing;
@@ -767,7 +918,7 @@ __device__ __forceinline__ void gemv_acc1(Smem sm, const Stream& st, int i, int 
   for (int u = 0; u < G; ++u) {
     if (u < g) {
       const int rs = rs0 + u < kRing ? rs0 + u : rs0 + u - kRing;
-      const char* sl = sm.ring + (size_t)rs * kTileBytes + wave * 2048 + lane * 16;
+      const char* sl = sm.ring + (size_t)rs * kSlotBytes + wave * 2048 + lane * 16;
       wv[u][0] = *reinterpret_cast<const uint4*>(sl);
       wv[u][1] = *reinterpret_cast<const uint4*>(sl + 1024);
     }
@@ -840,7 +991,7 @@ __device__ __forceinline__ float part_row(const float* part, int block, int q, i
 template <typename WT, int MT, class SegFn, class EpiFn>
 __device__ __forceinline__ void run_gemv(Smem sm, Stream& st, const Plan& cur, const Plan& nxt, XRegs<WT, MT>& xr,
                                          SegFn seg, EpiFn epi) {
-  constexpr int G = GroupOf<MT>::G;
+  constexpr int G = GroupOf<WT, MT>::G;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   st.mark(1);
   settle();
@@ -1117,9 +1268,6 @@ __device__ __forceinline__ float sum_groups(float v) {
 //    the score layout is already the operand layout P^T needs.
 // The four wave states are merged through LDS into the split's partial
 // (maximum stored in natural units).
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4_t*)(const_cast<char*>(p)));
@@ -1714,6 +1862,30 @@ __device__ __forceinline__ void load_x_lds(XRegs<WT, MT>& xr, const float* base,
   }
 }
 
+// x registers from LDS rows given by rowof(t) (the row offset of token t,
+// every offset valid; the token mask is applied to the results).  8 rows with
+// bf16 weights: each lane forms the offsets of its own two tokens.
+template <typename WT, int MT, class RowFn>
+__device__ __forceinline__ void load_x_rows(XRegs<WT, MT>& xr, const float* base, RowFn rowof, int wave, int lane,
+                                            int lrb) {
+  if constexpr (std::is_same<WT, uint16_t>::value && MT == 8) {
+    const int t4 = lane & 3, b = lane >> 2;
+    const int k0 = m8_kq(wave, lrb) + b * 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* s = base + rowof(t4 + 4 * h) + k0;
+#pragma unroll
+      for (int kc = 0; kc < 16; ++kc)
+        split_bf16x4(*reinterpret_cast<const float4*>(s + kc * 64), xr.hi[h][kc], xr.lo[h][kc]);
+    }
+  } else {
+    int ro[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ro[t] = rowof(t);
+    load_x_lds<WT, MT>(xr, base, ro, 0u, wave, lane, lrb);
+  }
+}
+
 // Shared activations a_s [M][S][F] -> LDS by DMA (whole KiB; F*4 bytes is a
 // multiple of 1 KiB), issued right after the RS -> RG barrier so that its
 // latency overlaps the routing step's load of the logits.
@@ -1747,10 +1919,7 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
         seg_all<MT>(sg, M);
         if (i < n1) {  // expert s of the shared down projection, all of this CU's j-blocks
           const int sx = i / nj;
-          int ro[MT];
-#pragma unroll
-          for (int t = 0; t < MT; ++t) ro[t] = (t * S + sx) * F;
-          load_x_lds<WT, MT>(xw, sm.xs, ro, sg.tmask, wave, lane, lrb);
+          load_x_rows<WT, MT>(xw, sm.xs, [&](int t) { return (t * S + sx) * F; }, wave, lane, lrb);
           sg.end = i + nj;
           sg.blk0 = 0;
           sg.accum = true;
@@ -1830,7 +1999,7 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
     }
   };
   if constexpr (MT == 1) {
-    constexpr int G = GroupOf<1>::G;
+    constexpr int G = GroupOf<WT, 1>::G;
     if (nj <= G && xl) {
       // One row: the union experts are its k experts, each expert's j-blocks
       // form one group, and the weighted partial sums of all experts stay in
@@ -1882,17 +2051,21 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
       [&](int i, Seg<MT>& sg) {
         const int u = i / nj;
         unsigned tm = 0;
-        int ro[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {  // uslot is -1 for rows beyond M
           const int sl = ms->uslot[u * kMaxRows + t];
           const int slc = sl < 0 ? 0 : sl;
           const float wt = ms->wts[min(t * k + slc, kMaxRows * kMaxTopK - 1)];
-          ro[t] = sl < 0 ? 0 : (t * k + sl) * F;
           sg.tw[t] = sl < 0 ? 0.f : wt;
           tm |= (sl < 0 ? 0u : 1u) << t;
         }
-        load_x_lds<WT, MT>(xr, xl ? sm.xs : a_g, ro, tm, wave, lane, lrb);
+        load_x_rows<WT, MT>(
+            xr, xl ? sm.xs : a_g,
+            [&](int t) {  // t may differ across lanes: the slot is read per lane
+              const int sl = ms->uslot[u * kMaxRows + t];
+              return sl < 0 ? 0 : (t * k + sl) * F;
+            },
+            wave, lane, lrb);
         sg.tmask = tm;
         sg.end = i + nj;
         sg.blk0 = 0;
@@ -1908,9 +2081,9 @@ template <typename WT, int MT, int QW>
 __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   Smem sm;
   sm.ring = smem_raw;
-  sm.xs = reinterpret_cast<float*>(smem_raw + (size_t)kRing * kTileBytes);
-  sm.part = reinterpret_cast<float*>(smem_raw + (size_t)kRing * kTileBytes + kXsBytes);
-  sm.misc = reinterpret_cast<Misc*>(smem_raw + (size_t)kRing * kTileBytes + kXsBytes + kPartBytes);
+  sm.xs = reinterpret_cast<float*>(smem_raw + (size_t)kRing * kSlotBytes);
+  sm.part = reinterpret_cast<float*>(smem_raw + (size_t)kRing * kSlotBytes + kXsBytes);
+  sm.misc = reinterpret_cast<Misc*>(smem_raw + (size_t)kRing * kSlotBytes + kXsBytes + kPartBytes);
   Misc* ms = sm.misc;
   const KParams& p = kp;
   // positions: range and distinctness within a sequence (every CU checks the

@@ -293,7 +293,7 @@ int mk_get_info(const mk_handle* h, mk_info* info) {
   if (!h || !info) return fail(MK_ERR_INVALID_ARG, "NULL argument");
   info->n_cu = h->n_cu;
   info->threads = mk::kThreads;
-  info->lds_bytes = h->ring_tiles * mk::kTileBytes + h->x_bytes + mk::kPartBytes + mk::kMiscBytes;
+  info->lds_bytes = h->ring_tiles * mk::kSlotBytes + h->x_bytes + mk::kPartBytes + mk::kMiscBytes;
   info->barriers_per_step = h->barriers;
   info->attn_splits = h->n_splits;
   info->workspace_bytes =
