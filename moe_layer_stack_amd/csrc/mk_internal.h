@@ -59,6 +59,7 @@ struct ActLayout {
   size_t a_s;     // [M][n_shared][F]  shared SwiGLU activations
   size_t a;       // [M][k][F]         routed SwiGLU activations (slot = top-k rank)
   size_t y_s;     // [M][d]            shared-expert down projection
+  size_t yp;      // [M][k][d]         routed down projections per top-k slot, weighted (rows > 1 only)
   size_t h2;      // [M][d]            layer output (next layer's input)
   size_t stride;  // bytes per layer
 };

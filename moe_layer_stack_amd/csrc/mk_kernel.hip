@@ -275,7 +275,7 @@ __device__ __forceinline__ void my_range(int n, int ncu, int& lo, int& hi) {
 // of static phases can be built before the phase starts, which is what lets
 // the ring run ahead across phase boundaries.
 
-enum PlanKind { PK_NONE = 0, PK_QKV, PK_ATTN, PK_WO, PK_RS, PK_RG, PK_DOWN };
+enum PlanKind { PK_NONE = 0, PK_QKV, PK_ATTN, PK_WO, PK_RS, PK_RG, PK_DOWN, PK_DOWNA };
 
 struct Plan {
   int kind;
@@ -286,7 +286,7 @@ struct Plan {
   int lo2;           // first unit of the second segment
   int lrb2, rpt2;    // second segment geometry (RS, RG)
   int fb_per;        // f-blocks per expert in the second segment
-  int nj;            // RG: shared-down units; DOWN: j-blocks per expert
+  int nj;            // RG: shared-down units; DOWN: this CU's j-blocks; DOWNA: j-blocks per expert
   int a0, a1;        // QKV: nq, nk; ATTN: p_lo, p_hi; RS: E; RG, DOWN: unused
   int d, F, S, U;
   const char* b0;
@@ -338,6 +338,10 @@ __device__ __forceinline__ TileSrc plan_tile(const Plan& P, int i, const Misc* m
     }
     case PK_DOWN: {  // expert-major: tile = u * nj + (jb - lo)
       const int u = i / P.nj, jb = P.lo + i % P.nj;
+      return TileSrc{P.b0 + (((size_t)ms->uni[u] * P.d + (size_t)jb * P.rpt) << P.lrb), kTileBytes};
+    }
+    case PK_DOWNA: {  // flat (union expert, j-block) index, expert-major
+      const int g = P.lo + i, u = g / P.nj, jb = g - u * P.nj;
       return TileSrc{P.b0 + (((size_t)ms->uni[u] * P.d + (size_t)jb * P.rpt) << P.lrb), kTileBytes};
     }
     default:
@@ -483,6 +487,30 @@ __device__ __forceinline__ Plan plan_down(const KParams& p, const Misc* ms, int 
   P.lo = lo;
   P.nj = hi - lo;
   P.n = (hi - lo) * P.U;
+  P.b0 = (const char*)layer_tab(p)[l].w_down;
+  return P;
+}
+
+// DOWN with several rows, first half: the (union expert, j-block) tiles of
+// all experts in one expert-major order, cut into contiguous ranges, so a CU
+// meets one or two experts; lo2 / n1 are this CU's output column blocks for
+// the second half.
+template <typename WT>
+__device__ __forceinline__ Plan plan_down_a(const KParams& p, const Misc* ms, int l) {
+  Plan P{};
+  P.kind = PK_DOWNA;
+  P.lrb = ilog2(p.F * (int)sizeof(WT));
+  P.rpt = kTileBytes >> P.lrb;
+  P.d = p.d;
+  P.U = ms->n_uni;
+  P.nj = p.d / P.rpt;
+  int lo, hi;
+  my_range(P.U * P.nj, p.n_cu, lo, hi);
+  P.lo = lo;
+  P.n = hi - lo;
+  my_range(P.nj, p.n_cu, lo, hi);
+  P.lo2 = lo;
+  P.n1 = hi - lo;
   P.b0 = (const char*)layer_tab(p)[l].w_down;
   return P;
 }
@@ -2075,6 +2103,95 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
       epilogue);
 }
 
+// DOWN with several rows, first half: this CU's contiguous range of the
+// (union expert, j-block) tiles, expert-major, so the x rows of an expert
+// (the activations of the rows routed to it) are loaded once per CU instead
+// of once per expert.  Each tile's weighted products for the routed rows go
+// to yp[t][slot][j]; the second half sums a row's slots per column.  The
+// residual h1 + y_s of the second half's columns goes to LDS here.
+template <typename WT, int MT>
+__device__ __forceinline__ void phase_down_a(const KParams& p, Smem sm, int l, Stream& st, const Plan& P,
+                                             const Plan& N) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int d = p.d, F = p.F, k = p.k, M = p.M;
+  const int nj = P.nj, rpt = P.rpt, lrb = P.lrb, lo = P.lo, n = P.n;
+  const float* h1 = layer_h1(p, l);
+  const float* a_g = act_f(p, l, p.al.a);    // [M][k][F]
+  const float* ys = act_f(p, l, p.al.y_s);   // [M][d]
+  float* yp = act_w(p, l, p.al.yp);          // [M][k][d]
+  const bool xl = (size_t)M * k * F * 4 <= (size_t)kXsBytes;
+  if (xl) dma_to_lds((char*)sm.xs, (const char*)a_g, M * k * F * 4, wave, lane);
+  zero_part(sm);
+  load_res(sm, h1, p.S > 0 ? ys : nullptr, d, P.lo2 * rpt, P.n1 * rpt, M);
+  wait_all();
+  __syncthreads();
+  const Misc* ms = sm.misc;
+  constexpr int kRound = kPartAcc / (kWaves * Slots<WT>::C * MT);
+  const int lrpt = 13 - lrb;  // log2 rows per tile
+  XRegs<WT, MT> xr;
+  int xu = -1;  // expert whose x rows the registers hold
+  run_gemv<WT, MT>(
+      sm, st, P, N, xr,
+      [&](int i, Seg<MT>& sg) {
+        const int u = (lo + i) / nj;
+        sg.end = min(min(n, (u + 1) * nj - lo), (i / kRound + 1) * kRound);
+        sg.blk0 = i % kRound;
+        sg.accum = false;
+        sg.round_end = sg.end == n || sg.end % kRound == 0;
+        sg.tmask = ms->umask[u];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {  // uslot is -1 for rows beyond M
+          const int sl = ms->uslot[u * kMaxRows + t];
+          sg.tw[t] = sl < 0 ? 0.f : ms->wts[t * k + sl];
+        }
+        if (u != xu) {
+          xu = u;
+          load_x_rows<WT, MT>(
+              xr, xl ? sm.xs : a_g,
+              [&](int t) {  // t may differ across lanes: the slot is read per lane
+                const int sl = ms->uslot[u * kMaxRows + t];
+                return sl < 0 ? 0 : (t * k + sl) * F;
+              },
+              wave, lane, lrb);
+        }
+      },
+      [&](int first, int last) {
+        for (int it = threadIdx.x; it < (last - first + 1) << lrpt; it += kThreads) {
+          const int b = it >> lrpt, r = it & (rpt - 1);
+          const int g = lo + first + b, u = g / nj, jb = g - u * nj;
+          float* dst = yp + (size_t)jb * rpt + r;
+          for (unsigned m = ms->umask[u]; m; m &= m - 1) {
+            const int t = __builtin_ctz(m);
+            const int sl = ms->uslot[u * kMaxRows + t];
+            st_dev(dst + ((size_t)t * k + sl) * d, part_row<WT, MT>(sm.part, b, r, lrb, t));
+          }
+        }
+      });
+}
+
+// DOWN with several rows, second half: h2[t][j] = h1 + y_s + the sum of
+// yp[t][slot][j] over the row's top-k slots, for this CU's output columns
+// [c0, c0 + ncol) (the residual is in LDS from the first half).
+__device__ __forceinline__ void phase_down_b(const KParams& p, Smem sm, int l, int c0, int ncol) {
+  const int d = p.d, k = p.k, M = p.M;
+  const float* yp = act_f(p, l, p.al.yp);
+  const bool last_layer = (l == p.L - 1);
+  float* h2 = last_layer ? p.hidden_out : act_w(p, l, p.al.h2);
+  const float* res = res_slice(sm);
+  for (int it = threadIdx.x; it < ncol * M; it += kThreads) {
+    const int t = it / ncol, c = it - t * ncol;
+    const float* src = yp + (size_t)t * k * d + c0 + c;
+    float v[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) v[s] = s < k ? src[(size_t)s * d] : 0.f;
+    float out = res[it];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) out += v[s];
+    if (last_layer) h2[(size_t)t * d + c0 + c] = out;
+    else st_dev(h2 + (size_t)t * d + c0 + c, out);
+  }
+}
+
 // ------------------------------------------------------------------ kernel
 
 template <typename WT, int MT, int QW>
@@ -2171,7 +2288,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
       rg_stage(p, sm, l);
       route_topk(p, sm, l);
       cur = plan_rg<WT>(p, ms, l, true);  // same first tiles as the prefetched plan
-      const Plan nxt = plan_down<WT>(p, ms, l);
+      const Plan nxt = MT == 1 ? plan_down<WT>(p, ms, l) : plan_down_a<WT>(p, ms, l);
       phase_rg<WT, MT>(p, sm, l, st, cur, nxt, xr_moe);
       MK_SYNC();
       st.advance(cur);
@@ -2179,10 +2296,20 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
     }
     {
       const Plan nxt = (l + 1 < p.L) ? (p.attn ? plan_qkv<WT>(p, l + 1) : plan_rs<WT>(p, l + 1)) : none;
-      phase_down<WT, MT>(p, sm, l, st, cur, nxt);
-      if (l + 1 < p.L) MK_SYNC();
-      st.advance(cur);
-      cur = nxt;
+      if constexpr (MT == 1) {
+        phase_down<WT, MT>(p, sm, l, st, cur, nxt);
+        if (l + 1 < p.L) MK_SYNC();
+        st.advance(cur);
+        cur = nxt;
+      } else {
+        const int c0 = cur.lo2 * cur.rpt, ncol = cur.n1 * cur.rpt;
+        phase_down_a<WT, MT>(p, sm, l, st, cur, nxt);
+        MK_SYNC();
+        st.advance(cur);
+        cur = nxt;
+        phase_down_b(p, sm, l, c0, ncol);  // no tiles: the next layer's first tiles stay in flight
+        if (l + 1 < p.L) MK_SYNC();
+      }
     }
   }
 #undef MK_SYNC

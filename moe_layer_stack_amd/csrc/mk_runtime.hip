@@ -210,7 +210,9 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
       return fail(MK_ERR_UNSUPPORTED, "d_model * rows too large for %d CUs", prop.multiProcessorCount);
     }
   }
-  h->barriers = c.n_layers * (c.has_attn ? 6 : 3) - 1;
+  // several rows: the routed down projection runs in two phases (expert-major
+  // products, then the per-column sum), one more barrier per layer
+  h->barriers = c.n_layers * ((c.has_attn ? 6 : 3) + (M > 1 ? 1 : 0)) - 1;
   // LDS: fixed carve-up (ring, x staging, per-row partial sums, misc)
   h->x_bytes = mk::kXsBytes;
   h->ring_tiles = mk::kRing;
@@ -232,6 +234,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   al.a_s = take((size_t)M * S * F * 4);
   al.a = take((size_t)M * k * F * 4);
   al.y_s = take((size_t)M * d * 4);
+  al.yp = take(M > 1 ? (size_t)M * k * d * 4 : 0);
   al.h2 = take((size_t)M * d * 4);
   al.stride = align256(off);
   h->al = al;
