@@ -369,6 +369,15 @@ __device__ __forceinline__ Plan plan_qkv(const KParams& p, int l) {
 }
 
 // attention split owned by this CU (tasks never outnumber CUs)
+// CU -> attention task (sequence, kv head, split).  Workgroups are dealt to
+// the 8 XCDs round-robin; tasks are numbered XCD by XCD, so the splits of one
+// (sequence, kv head), consecutive tasks, share an XCD when the split count
+// divides the CUs per XCD, and their partial records meet in that XCD's L2.
+__device__ __forceinline__ int attn_task(int ncu) {
+  const int b = blockIdx.x;
+  return (ncu & 7) ? b : (b & 7) * (ncu >> 3) + (b >> 3);
+}
+
 // trail: one row per sequence (decode); its new position, the sequence's
 // last, is attended from the copy in LDS instead of a cache tile, and the
 // split S-1 owns it (P.U = 1, P.F = its position).  The cached positions are
@@ -377,7 +386,7 @@ __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int 
   Plan P{};
   P.kind = PK_ATTN;
   const int S = p.n_splits;
-  const int task = blockIdx.x;
+  const int task = attn_task(p.n_cu);
   if (task >= p.n_seq * p.G * S) return P;
   const int seq = task / (p.G * S), g = (task / S) % p.G, s = task % S;
   int maxpos = 0;
@@ -1319,7 +1328,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   uint16_t* nvb = nkb + kMaxRows * 128;
   static_assert((NQ * 128 + 2 * kMaxRows * 128 + kWaves * NQ * kPartStride) * 4 + 2 * kMaxRows * 128 * 2 <= kXsBytes,
                 "attention scratch exceeds the x region");
-  const int task = blockIdx.x;
+  const int task = attn_task(p.n_cu);
   const bool active = task < ntask;
   const int seq = active ? task / (p.G * S) : 0, g = active ? (task / S) % p.G : 0, s = active ? task % S : 0;
   const int p_lo = P.a0, p_hi = P.a1;
@@ -1531,7 +1540,7 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
   float* newk = sm.xs + kMaxQ * 128;          // [rps][hd] this step's k rows (bf16-rounded)
   float* newv = newk + kMaxRows * 128;        // [rps][hd]
   float* coef = newv + kMaxRows * 128;        // [Q][S] combine weights
-  const int task = blockIdx.x;
+  const int task = attn_task(p.n_cu);
   const bool active = task < ntask;
   const int seq = active ? task / (p.G * S) : 0, g = active ? (task / S) % p.G : 0, s = active ? task % S : 0;
   const int p_lo = P.a0, p_hi = P.a1;
