@@ -907,14 +907,19 @@ __device__ __forceinline__ void gemv_group<uint16_t, 8>(Smem sm, const Stream& s
   const int u = r < g ? r : 0;  // rows past the group read row 0; their sums are dropped
   const int rs = rs0 + u < kRing ? rs0 + u : rs0 + u - kRing;
   const char* wp = sm.ring + (size_t)rs * kSlotBytes + wave * 2048 + b * 8;
+  // All 16 reads are issued before the first product (a fence keeps the
+  // scheduler from sinking them): one LDS round trip per group, not eight.
+  s16x4_t w[16];
+#pragma unroll
+  for (int kc = 0; kc < 16; ++kc) w[kc] = *reinterpret_cast<const s16x4_t*>(wp + kc * 128);
+  __builtin_amdgcn_sched_barrier(0);
   f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < 16; ++kc) {
-    const s16x4_t w = *reinterpret_cast<const s16x4_t*>(wp + kc * 128);
-    d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.hi[0][kc], w, d0, 0, 0, 0);
-    d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.lo[0][kc], w, d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.hi[1][kc], w, d1, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.lo[1][kc], w, d1, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.hi[0][kc], w[kc], d0, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.lo[0][kc], w[kc], d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.hi[1][kc], w[kc], d1, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.lo[1][kc], w[kc], d1, 0, 0, 0);
   }
   float v[8];
 #pragma unroll
