@@ -921,27 +921,40 @@ __device__ __forceinline__ void gemv_group<uint16_t, 8>(Smem sm, const Stream& s
     d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.hi[1][kc], w[kc], d1, 0, 0, 0);
     d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xr.lo[1][kc], w[kc], d1, 0, 0, 0);
   }
-  float v[8];
+  // Sum over the 16 blocks (lane bits 2-5) in halving steps, each leaving
+  // half of the token values in a lane, summed with its partner's copy:
+  // bit 5 (tokens t < 4 stay where the bit is clear), bit 4, then bit 2 by a
+  // row rotation by 4 (the lanes it pairs always differ in bit 2) and a plain
+  // sum over bit 3 by a rotation by 8.  Lane l with bit 3 clear then holds
+  // token t = 4*bit5 + 2*bit4 + bit2 of row r.
+  float w4[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    v[t] = d0[t];
-    v[t + 4] = d1[t];
-  }
+  for (int i = 0; i < 4; ++i) w4[i] = swap32_sum(d0[i], d1[i]);
+  float w2[2];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {  // over the 16 blocks: lane bits 2, 3 (rotations), 4, 5 (swaps)
-    float x = v[t];
-    x += dpp<kDppRor4>(x);
-    x += dpp<kDppRor8>(x);
-    v[t] = sum_rows(x);
-  }
-  if (b == 0 && r < g) {
-    float* dst = sm.part + (size_t)(blk0 + r) * (kWaves * 8) + wave * 8;
+  for (int i = 0; i < 2; ++i) w2[i] = swap16_sum(w4[i], w4[2 + i]);
+  const bool b2 = (lane >> 2) & 1;
+  float x = (b2 ? w2[1] : w2[0]) + dpp<kDppRor4>(b2 ? w2[0] : w2[1]);
+  x += dpp<kDppRor8>(x);
+  if (((lane >> 3) & 1) == 0 && r < g) {
+    const bool b4 = (lane >> 4) & 1, b5 = (lane >> 5) & 1;
+    const int t = 4 * b5 + 2 * b4 + b2;
+    // the token's weight by a select tree on the lane bits; the values pass
+    // through an empty asm so that the selects are not folded back into an
+    // indexed access, which would go through scratch memory
+    float q[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float val = ((tmask >> t) & 1u) ? v[t] * tw[t] : 0.f;
-      if (accum) dst[t] += val;
-      else dst[t] = val;
+    for (int i = 0; i < 8; ++i) {
+      q[i] = tw[i];
+      asm volatile("" : "+v"(q[i]));
     }
+    const float a0 = b2 ? q[1] : q[0], a1 = b2 ? q[3] : q[2];
+    const float a2 = b2 ? q[5] : q[4], a3 = b2 ? q[7] : q[6];
+    const float twt = b5 ? (b4 ? a3 : a2) : (b4 ? a1 : a0);
+    const float val = ((tmask >> t) & 1u) ? x * twt : 0.f;
+    float* dst = sm.part + (size_t)(blk0 + r) * (kWaves * 8) + wave * 8 + t;
+    if (accum) *dst += val;
+    else *dst = val;
   }
 }
 
