@@ -128,6 +128,20 @@ __device__ __forceinline__ void g2l(const void* g, unsigned lds_wave_base) {
       : "memory", "m0");
 }
 
+// Two 1 KiB chunks: g -> LDS base and g + 1024 -> base + 1024 (the
+// instruction offset applies to the global and the LDS address alike), one
+// M0 write for both.
+__device__ __forceinline__ void g2l2(const void* g, unsigned lds_wave_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off nt\n\t"
+      "global_load_lds_dwordx4 %0, off offset:1024 nt"
+      :
+      : "v"(g), "s"(m0)
+      : "memory", "m0");
+}
+
 // s_waitcnt with compiler memory-barrier semantics
 #define MK_WAIT_ASM(text) asm volatile(text ::: "memory")
 __device__ __forceinline__ void wait_all() { MK_WAIT_ASM("s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)"); }
@@ -553,8 +567,12 @@ __device__ __forceinline__ void issue_tile(const Win& w, int j, unsigned slot_ld
   const unsigned lo = __builtin_amdgcn_readlane(w.lo, idx);
   const unsigned hi = __builtin_amdgcn_readlane(w.hi, idx);
   const char* g = reinterpret_cast<const char*>(((unsigned long long)(hi & 0x07ffffffu) << 32) | lo);
-  const int valid = kTileBytes - (int)((hi >> 27) << 8);
   const int off0 = wave * 2048 + lane * 16;
+  if ((hi >> 27) == 0) {  // a whole tile (the common case; wave-uniform)
+    g2l2(g + off0, slot_lds + wave * 2048);
+    return;
+  }
+  const int valid = kTileBytes - (int)((hi >> 27) << 8);
   const int off1 = off0 + 1024;
   g2l(g + (off0 < valid ? off0 : 0), slot_lds + wave * 2048);
   g2l(g + (off1 < valid ? off1 : 0), slot_lds + wave * 2048 + 1024);
