@@ -277,10 +277,31 @@ __device__ __forceinline__ const float* layer_in(const KParams& p, int l) {
 __device__ __forceinline__ const float* layer_h1(const KParams& p, int l) {
   return p.attn ? act_f(p, l, p.al.h1) : layer_in(p, l);
 }
-// balanced split of n items over the grid
+// q = a / b, r = a % b for 0 <= a < 2^24, 1 <= b and a / b < 2^22: the float
+// estimate of the quotient is within one of the truth, and one correction
+// each way makes it exact.  A few instructions instead of the generic
+// integer division's dozens (code size matters: the kernel streams through
+// more instructions per layer than the instruction cache holds).
+struct QR {
+  int q, r;
+};
+__device__ __forceinline__ QR divmod_small(int a, int b) {
+  int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+  int r = a - q * b;
+  if (r < 0) {
+    q -= 1;
+    r += b;
+  }
+  if (r >= b) {
+    q += 1;
+    r -= b;
+  }
+  return QR{q, r};
+}
+// balanced split of n items over the grid (blockIdx * n stays below 2^32)
 __device__ __forceinline__ void my_range(int n, int ncu, int& lo, int& hi) {
-  lo = (int)(((long long)blockIdx.x * n) / ncu);
-  hi = (int)(((long long)(blockIdx.x + 1) * n) / ncu);
+  lo = (int)((blockIdx.x * (unsigned)n) / (unsigned)ncu);
+  hi = (int)(((blockIdx.x + 1) * (unsigned)n) / (unsigned)ncu);
 }
 
 // ------------------------------------------------------------------ phase plans
@@ -337,25 +358,30 @@ __device__ __forceinline__ TileSrc plan_tile(const Plan& P, int i, const Misc* m
       }
       const int k = i - P.n1;
       const int pj = P.lo2 + (k >> 1);
-      const int sx = pj / P.fb_per, fb = pj % P.fb_per;
+      const QR sf = divmod_small(pj, P.fb_per);
+      const int sx = sf.q, fb = sf.r;
       return TileSrc{((k & 1) ? P.b2 : P.b1) + (((size_t)sx * P.F + (size_t)fb * P.rpt) << P.lrb), kTileBytes};
     }
     case PK_RG: {
       if (i < P.n1) {  // shared down, expert-major: tile = s * nj + unit
-        const int s = i / P.nj, unit = P.lo + i % P.nj;
+        const QR su = divmod_small(i, P.nj);
+        const int s = su.q, unit = P.lo + su.r;
         return TileSrc{P.b0 + (((size_t)s * P.d + (size_t)unit * P.rpt) << P.lrb), kTileBytes};
       }
       const int k = i - P.n1;
       const int pj = P.lo2 + (k >> 1);
-      const int e = ms->uni[pj / P.fb_per], fb = pj % P.fb_per;
+      const QR ef = divmod_small(pj, P.fb_per);
+      const int e = ms->uni[ef.q], fb = ef.r;
       return TileSrc{((k & 1) ? P.b2 : P.b1) + (((size_t)e * P.F + (size_t)fb * P.rpt2) << P.lrb2), kTileBytes};
     }
     case PK_DOWN: {  // expert-major: tile = u * nj + (jb - lo)
-      const int u = i / P.nj, jb = P.lo + i % P.nj;
+      const QR uj = divmod_small(i, P.nj);
+      const int u = uj.q, jb = P.lo + uj.r;
       return TileSrc{P.b0 + (((size_t)ms->uni[u] * P.d + (size_t)jb * P.rpt) << P.lrb), kTileBytes};
     }
     case PK_DOWNA: {  // flat (union expert, j-block) index, expert-major
-      const int g = P.lo + i, u = g / P.nj, jb = g - u * P.nj;
+      const QR uj = divmod_small(P.lo + i, P.nj);
+      const int u = uj.q, jb = uj.r;
       return TileSrc{P.b0 + (((size_t)ms->uni[u] * P.d + (size_t)jb * P.rpt) << P.lrb), kTileBytes};
     }
     default:
@@ -408,7 +434,7 @@ __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int 
   const bool tr = trail && p.rps == 1;
   const int npos = tr ? maxpos : maxpos + 1;  // positions read from the cache
   const int ntile = (npos + kAttnTile - 1) / kAttnTile;
-  const int t_lo = (int)(((long long)s * ntile) / S), t_hi = (int)(((long long)(s + 1) * ntile) / S);
+  const int t_lo = (int)(((unsigned)s * ntile) / (unsigned)S), t_hi = (int)(((unsigned)(s + 1) * ntile) / (unsigned)S);
   P.a0 = min(t_lo * kAttnTile, npos);
   P.a1 = min(t_hi * kAttnTile, npos);
   P.n = 2 * (t_hi - t_lo);
@@ -1175,9 +1201,11 @@ __device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, in
   float* scr = sm.xs;  // [S][nw]
   Misc* ms = sm.misc;
   auto word = [&](int it) -> int {  // byte offset of word it
-    const int z = it / nw, w = it - z * nw;
-    const int q = w < 2 * nq ? q0 + (w >> 1) : (o0 + w - 2 * nq) / hd;
-    const int c = w < 2 * nq ? (w & 1) : 4 + (o0 + w - 2 * nq) % hd;
+    const QR zw = divmod_small(it, nw);
+    const int z = zw.q, w = zw.r;
+    const QR od = divmod_small(o0 + w - 2 * nq, hd);
+    const int q = w < 2 * nq ? q0 + (w >> 1) : od.q;
+    const int c = w < 2 * nq ? (w & 1) : 4 + od.r;
     return ((z * Q + q) * kPartStride + c) * 8;
   };
   if (threadIdx.x == 0) ms->last = 0;  // set on a time-out (read after the first synchronisation)
