@@ -388,6 +388,19 @@ __device__ __forceinline__ TileSrc plan_tile(const Plan& P, int i, const Misc* m
       return TileSrc{nullptr, 0};
   }
 }
+// plan_tile for a plan of kind K known at compile time (the switch folds to
+// one case), or of any kind for K = kAnyKind
+constexpr int kAnyKind = -1;
+template <int K>
+__device__ __forceinline__ TileSrc plan_tile_k(const Plan& P, int i, const Misc* ms) {
+  if constexpr (K == kAnyKind) {
+    return plan_tile(P, i, ms);
+  } else {
+    Plan Q = P;
+    Q.kind = K;
+    return plan_tile(Q, i, ms);
+  }
+}
 
 template <typename WT>
 __device__ __forceinline__ Plan plan_qkv(const KParams& p, int l) {
@@ -575,10 +588,11 @@ struct Win {
   int w0;
 };
 constexpr int kNoWin = -(1 << 24);
+template <int K>
 __device__ __forceinline__ Win build_win(const Plan& P, int w0, const Misc* ms, int lane) {
   const int j = w0 + lane;
   TileSrc t{nullptr, kTileBytes};
-  if (j < P.n) t = plan_tile(P, j, ms);
+  if (j < P.n) t = plan_tile_k<K>(P, j, ms);
   const unsigned long long a = (unsigned long long)(uintptr_t)t.g;
   Win w;
   w.lo = (unsigned)a;
@@ -628,7 +642,9 @@ struct Stream {
   __device__ __forceinline__ char* slot(Smem sm, int j) const {
     return sm.ring + (size_t)((slot0 + j) % kRing) * kSlotBytes;
   }
-  // issue while ring slots are free; `consumed` tiles of cur are done
+  // issue while ring slots are free; `consumed` tiles of cur are done.  KC,
+  // KN: the kinds of cur and nxt when known at compile time
+  template <int KC, int KN>
   __device__ __forceinline__ void fill(Smem sm, const Plan& cur, const Plan& nxt, int consumed, int wave,
                                        int lane) {
     // The slots being refilled held tiles whose reads this wave has already
@@ -638,11 +654,11 @@ struct Stream {
       const unsigned s = ring_lds + (unsigned)islot * kSlotBytes;
       islot = islot == kRing - 1 ? 0 : islot + 1;
       if (issued < cur.n) {
-        if ((unsigned)(issued - wc.w0) >= 64u) wc = build_win(cur, issued, sm.misc, lane);
+        if ((unsigned)(issued - wc.w0) >= 64u) wc = build_win<KC>(cur, issued, sm.misc, lane);
         issue_tile(wc, issued, s, wave, lane);
       } else {
         const int j = issued - cur.n;
-        if ((unsigned)(j - wn.w0) >= 64u) wn = build_win(nxt, j, sm.misc, lane);
+        if ((unsigned)(j - wn.w0) >= 64u) wn = build_win<KN>(nxt, j, sm.misc, lane);
         issue_tile(wn, j, s, wave, lane);
       }
     }
@@ -1087,14 +1103,14 @@ __device__ __forceinline__ float part_row(const float* part, int block, int q, i
 // run starting at tile i (and may reload the x registers); after a run with
 // round_end set, all waves synchronise and epi(first, last) runs over the
 // round's tiles.  The stream keeps issuing `nxt`'s tiles meanwhile.
-template <typename WT, int MT, class SegFn, class EpiFn>
+template <typename WT, int MT, int KC, int KN, class SegFn, class EpiFn>
 __device__ __forceinline__ void run_gemv(Smem sm, Stream& st, const Plan& cur, const Plan& nxt, XRegs<WT, MT>& xr,
                                          SegFn seg, EpiFn epi) {
   constexpr int G = GroupOf<WT, MT>::G;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   st.mark(1);
   settle();
-  st.fill(sm, cur, nxt, 0, wave, lane);
+  st.fill<KC, KN>(sm, cur, nxt, 0, wave, lane);
   int round_first = 0;
   for (int i = 0; i < cur.n;) {
     Seg<MT> sg;
@@ -1103,7 +1119,7 @@ __device__ __forceinline__ void run_gemv(Smem sm, Stream& st, const Plan& cur, c
       const int g = min(G, sg.end - j);
       st.wait(j + g - 1);
       gemv_group<WT, MT>(sm, st, j, g, xr, sg.tmask, sg.tw, sg.blk0 + (j - i), sg.accum, wave, lane);
-      st.fill(sm, cur, nxt, j + g, wave, lane);
+      st.fill<KC, KN>(sm, cur, nxt, j + g, wave, lane);
     }
     if (sg.round_end) {
       __syncthreads();
@@ -1164,7 +1180,7 @@ __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stre
   constexpr int kRound = kPartAcc / (kWaves * Slots<WT>::C * MT);
   const Misc* ms = sm.misc;
   const int rpt = P.rpt, lo = P.lo, lrb = P.lrb, n = P.n;
-  run_gemv<WT, MT>(
+  run_gemv<WT, MT, PK_QKV, PK_ATTN>(
       sm, st, P, N, xr, [&](int i, Seg<MT>& sg) { seg_rounds<MT>(sg, i, 0, n, kRound, M); },
       [&](int first, int last) {
         const int nr = (last - first + 1) * rpt;
@@ -1506,7 +1522,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   };
   st.mark(1);
   settle();
-  st.fill(sm, P, N, 0, wave, lane);
+  st.fill<PK_ATTN, PK_WO>(sm, P, N, 0, wave, lane);
   const int nt = P.n / 2;  // position tiles
   for (int t = 0; t < nt; t += 2) {
     const bool hb = t + 1 < nt;
@@ -1523,7 +1539,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
       if (hb) patch(kb, vb, j0b);
     }
     step(ka, kb, va, vb, 256, j0a, j0b, qlim);
-    st.fill(sm, P, N, last + 1, wave, lane);
+    st.fill<PK_ATTN, PK_WO>(sm, P, N, last + 1, wave, lane);
   }
   if (P.U && wave == 0) {  // the trailing row, from its bf16 copy in LDS (rows r > 0 masked)
     const char* kr = reinterpret_cast<const char*>(nkb);
@@ -1673,11 +1689,11 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
   }
   st.mark(1);
   settle();
-  st.fill(sm, P, N, 0, wave, lane);
+  st.fill<PK_ATTN, PK_WO>(sm, P, N, 0, wave, lane);
   for (int i = 0; i < P.n; ++i) {
     st.wait(i);
     __syncthreads();  // tile i landed for every wave; every wave is done with tile i-1
-    st.fill(sm, P, N, i, wave, lane);
+    st.fill<PK_ATTN, PK_WO>(sm, P, N, i, wave, lane);
     const char* slot = st.slot(sm, i);
     const int t0 = p_lo + (i >> 1) * kAttnTile;
     const bool is_v = (i & 1) != 0;
@@ -1735,7 +1751,7 @@ __device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Str
       }
     }
   }
-  st.fill(sm, P, N, P.n, wave, lane);
+  st.fill<PK_ATTN, PK_WO>(sm, P, N, P.n, wave, lane);
   st.mark(2);
   if (!active) return;
   // sum the 4 position groups; lanes 0-15 hold acc for dims d0..d0+7
@@ -1777,7 +1793,7 @@ __device__ __forceinline__ void phase_wo(const KParams& p, Smem sm, int l, Strea
   __syncthreads();
   constexpr int kRound = kPartAcc / (kWaves * Slots<WT>::C * MT);
   const float* res = res_slice(sm);
-  run_gemv<WT, MT>(
+  run_gemv<WT, MT, PK_WO, PK_RS>(
       sm, st, P, N, xr, [&](int i, Seg<MT>& sg) { seg_rounds<MT>(sg, i, 0, n, kRound, M); },
       [&](int first, int last) {
         const int nr = (last - first + 1) * rpt;
@@ -1810,7 +1826,7 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
   constexpr int kRound = (kPartAcc / (kWaves * Slots<WT>::C * MT)) & ~1;  // even: a pair stays in one round
   const Misc* ms = sm.misc;
   const int rpt = P.rpt, lrb = P.lrb, n1 = P.n1, n = P.n, r_lo = P.lo, p_lo = P.lo2, fb_per = P.fb_per;
-  run_gemv<WT, MT>(
+  run_gemv<WT, MT, PK_RS, PK_RG>(
       sm, st, P, N, xr,
       [&](int i, Seg<MT>& sg) {
         if (i < n1) seg_rounds<MT>(sg, i, 0, n1, kRound, M);
@@ -2014,7 +2030,7 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
   const int n1 = P.n1, n = P.n, nj = P.nj, lrb = P.lrb, lrb2 = P.lrb2, rpt = P.rpt, rpt2 = P.rpt2;
   const int fb_per = P.fb_per, sd_lo = P.lo, p_lo = P.lo2;
   XRegs<WT, MT> xw;  // a_s rows for the shared-down tiles, then y
-  run_gemv<WT, MT>(
+  run_gemv<WT, MT, PK_RG, MT == 1 ? PK_DOWN : PK_DOWNA>(
       sm, st, P, N, xw,
       [&](int i, Seg<MT>& sg) {
         seg_all<MT>(sg, M);
@@ -2123,7 +2139,7 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
       for (int v = 0; v < G * C; ++v) pacc[v] = 0.f;
       st.mark(1);
       settle();
-      st.fill(sm, P, N, 0, wave, lane);
+      st.fill<PK_DOWN, kAnyKind>(sm, P, N, 0, wave, lane);
       ldx(xa, 0);
       for (int u = 0; u < (nj > 0 ? U : 0); ++u) {
         if (u + 1 < U) ldx(xb, u + 1);
@@ -2131,7 +2147,7 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
         const int j = u * nj;
         st.wait(j + nj - 1);
         gemv_acc1<WT>(sm, st, j, nj, xa, tw, pacc, wave, lane);
-        st.fill(sm, P, N, j + nj, wave, lane);
+        st.fill<PK_DOWN, kAnyKind>(sm, P, N, j + nj, wave, lane);
         xa = xb;
       }
       const float r = xreduce<G * C>(pacc, lane);
@@ -2147,7 +2163,7 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
     }
   }
   XRegs<WT, MT> xr;
-  run_gemv<WT, MT>(
+  run_gemv<WT, MT, PK_DOWN, kAnyKind>(
       sm, st, P, N, xr,
       [&](int i, Seg<MT>& sg) {
         const int u = i / nj;
@@ -2203,7 +2219,7 @@ __device__ __forceinline__ void phase_down_a(const KParams& p, Smem sm, int l, S
   const int lrpt = 13 - lrb;  // log2 rows per tile
   XRegs<WT, MT> xr;
   int xu = -1;  // expert whose x rows the registers hold
-  run_gemv<WT, MT>(
+  run_gemv<WT, MT, PK_DOWNA, kAnyKind>(
       sm, st, P, N, xr,
       [&](int i, Seg<MT>& sg) {
         const int u = (lo + i) / nj;
