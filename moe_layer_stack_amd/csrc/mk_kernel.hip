@@ -195,7 +195,6 @@ struct Misc {
   unsigned umask[kMaxExperts];                 // union expert u: rows routed to it
   signed char uslot[kMaxExperts * kMaxRows];   // [u][t]: top-k slot of expert u in row t, or -1
   float rope[kMaxRows * 64 * 2];  // (cos, sin) per row and frequency (head_dim 128)
-  float zs[kMaxRows * kMaxExperts];  // router logits of the step's rows
 };
 static_assert(sizeof(Misc) <= kMiscBytes, "misc region too small");
 
@@ -1868,44 +1867,59 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
   const int E = p.E, k = p.k, M = p.M;
   const float* logits = act_f(p, l, p.al.logits);
   Misc* ms = sm.misc;
-  for (int it = threadIdx.x; it < M * kMaxExperts; it += kThreads) {
-    const int t = it / kMaxExperts, e = it % kMaxExperts;
-    ms->zs[it] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
-  }
-  __syncthreads();
   // rank[t][e]: top-k slot of expert e in row t, or -1.  Kept in the
   // epilogue residual slice of the part region, which is free until DOWN.
   int* rank_tab = reinterpret_cast<int*>(res_slice(sm));
   static_assert(kMaxRows * kMaxExperts <= kResFloats, "rank table does not fit");
-  // Thread (e, part): expert e against the quarter `part` of the row's
-  // logits; the four partial ranks and maxima meet in the lane quad.
-  {
-    const int e = threadIdx.x >> 2, part = threadIdx.x & 3;
-    for (int t = 0; t < M; ++t) {
-      const float* zr = ms->zs + t * kMaxExperts;
-      const float z = zr[e];
-      int r = 0;
-      float zm = -INFINITY;
+  // Item (t, e) = it = 64 t + e: one wave holds whole rows, a lane one expert.
+  // Sort key: the logit's bits made order-preserving as an unsigned integer,
+  // above 63 - e, so that equal logits rank the lower id first and all keys
+  // of a row differ; rank = number of larger keys in the row.  The keys sit
+  // in the GEMV partial-sum region, unused until the phase's GEMV starts.
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(sm.part);
+  static_assert(kMaxRows * kMaxExperts * 8 <= kPartAcc * 4, "key table does not fit");
+  constexpr int kItems = kMaxRows * kMaxExperts / kThreads;
+  float zi[kItems], zmi[kItems];
+  unsigned long long ki[kItems];
 #pragma unroll
-      for (int jj = 0; jj < kMaxExperts / 4; jj += 4) {
-        const int j = part * (kMaxExperts / 4) + jj;
-        const float4 o = *reinterpret_cast<const float4*>(zr + j);
-        const int dd = e - j;  // expert j + c ranks first on a tie when c < dd
-        r += (o.x > z || (o.x == z && 0 < dd)) + (o.y > z || (o.y == z && 1 < dd)) +
-             (o.z > z || (o.z == z && 2 < dd)) + (o.w > z || (o.w == z && 3 < dd));
-        zm = fmaxf(zm, fmaxf(fmaxf(o.x, o.y), fmaxf(o.z, o.w)));
+  for (int q = 0; q < kItems; ++q) {
+    const int it = threadIdx.x + q * kThreads;
+    const int t = it >> 6, e = it & 63;
+    const float z = (t < M && e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+    unsigned u = __float_as_uint(z + 0.0f);  // -0 counts as +0
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    ki[q] = ((unsigned long long)u << 32) | (unsigned)(63 - e);
+    keys[it] = ki[q];
+    // row maximum over the wave
+    float m = z;
+    m = fmaxf(m, dpp<kDppXor1>(m));
+    m = fmaxf(m, dpp<kDppXor2>(m));
+    m = fmaxf(m, dpp<kDppRor4>(m));
+    m = fmaxf(m, dpp<kDppRor8>(m));
+    auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    zmi[q] = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    zi[q] = z;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int it = threadIdx.x + q * kThreads;
+    const int t = it >> 6, e = it & 63;
+    if (t < M) {
+      const unsigned long long* kr = keys + (it & ~63);
+      int r = 0;
+#pragma unroll 8
+      for (int j = 0; j < kMaxExperts; j += 2) {
+        const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(kr + j);
+        r += (kk.x > ki[q] ? 1 : 0) + (kk.y > ki[q] ? 1 : 0);
       }
-      r += __builtin_amdgcn_update_dpp(0, r, kDppXor1, 0xF, 0xF, false);
-      r += __builtin_amdgcn_update_dpp(0, r, kDppXor2, 0xF, 0xF, false);
-      zm = fmaxf(zm, dpp<kDppXor1>(zm));
-      zm = fmaxf(zm, dpp<kDppXor2>(zm));
       const bool sel = e < E && r < k;
-      if (part == 0) {
-        rank_tab[t * kMaxExperts + e] = sel ? r : -1;
-        if (sel) {
-          ms->ids[t * k + r] = e;
-          ms->wts[t * k + r] = __expf(z - zm);  // normalised below
-        }
+      rank_tab[it] = sel ? r : -1;
+      if (sel) {
+        ms->ids[t * k + r] = e;
+        ms->wts[t * k + r] = __expf(zi[q] - zmi[q]);  // normalised below
       }
     }
   }
