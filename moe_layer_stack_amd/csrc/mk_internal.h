@@ -17,7 +17,8 @@ constexpr int kMaxRows = 8;             // M
 constexpr int kMaxExperts = 64;         // E (one lane per expert in top-k)
 constexpr int kMaxTopK = 8;
 constexpr int kMaxShared = 4;
-constexpr int kMaxQ = 32;               // query vectors per attention task
+constexpr int kMaxQ = 32;               // query vectors per (sequence, kv head): rows_per_seq * H / G
+constexpr int kMaxQTask = 16;           // query vectors per attention task (one 16-wide MFMA operand)
 constexpr int kAttnTile = 32;           // positions per KV tile (hd = 128 bf16 -> 8 KB)
 constexpr int kLdsTotal = 160 * 1024;
 constexpr int kPartBytes = 16 * 1024;
@@ -84,7 +85,8 @@ struct KParams {
   int attn, has_bias, wide;  // wide: weights are fp32
   float eps, theta;
   int n_splits;              // KV splits per (seq, kv head)
-  int q_per_task;            // rps * (H / G)
+  int q_per_task;            // query vectors per attention task: rps * (H / G) / q_groups
+  int q_groups;              // attention tasks per (seq, kv head, split), each with its own queries
   // launch geometry / LDS carve-up
   int n_cu;
   int ring_tiles;

@@ -437,10 +437,10 @@ __device__ __forceinline__ int attn_task(int ncu) {
 __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int l, bool trail) {
   Plan P{};
   P.kind = PK_ATTN;
-  const int S = p.n_splits;
+  const int S = p.n_splits, QG = p.q_groups;
   const int task = attn_task(p.n_cu);
-  if (task >= p.n_seq * p.G * S) return P;
-  const int seq = task / (p.G * S), g = (task / S) % p.G, s = task % S;
+  if (task >= p.n_seq * p.G * QG * S) return P;
+  const int seq = task / (p.G * QG * S), g = (task / (QG * S)) % p.G, s = task % S;
   int maxpos = 0;
   for (int rr = 0; rr < p.rps; ++rr) maxpos = max(maxpos, ms->pos[seq * p.rps + rr]);
   const bool tr = trail && p.rps == 1;
@@ -1200,7 +1200,7 @@ __device__ __forceinline__ void phase_qkv(const KParams& p, Smem sm, int l, Stre
 // reads again until every word carries this launch's tag (no counter, no
 // last arriver).  Thread = (output, group of splits); the groups of an output
 // are neighbouring lanes, merged by butterfly shuffles.
-__device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, int seq, int g, int s, int Q) {
+__device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, int seq, int g, int qg, int s, int Q) {
   const int S = p.n_splits, HG = p.H / p.G, rps = p.rps, hd = p.hd;
   const int nout = Q * hd;
   const int nper = (nout + S - 1) / S;
@@ -1210,7 +1210,7 @@ __device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, in
   const int nw = 2 * nq + (o1 - o0);  // words per split: (m, l) per query, then the acc slice
   const int nload = S * nw;
   const tagword_t* rec0 = reinterpret_cast<const tagword_t*>(act_f(p, l, p.al.part)) +
-                          (size_t)((seq * p.G + g) * S) * Q * kPartStride;
+                          (size_t)(((seq * p.G + g) * p.q_groups + qg) * S) * Q * kPartStride;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<tagword_t*>(rec0), (short)0, S * Q * kPartStride * 8, kBufferDword3);
   float* scr = sm.xs;  // [S][nw]
@@ -1283,7 +1283,8 @@ __device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, in
       A += __shfl_xor(A, sh);
     }
     if (t < nouts * ZG && zg == 0) {
-      const int row = seq * rps + q / HG, head = g * HG + q % HG;
+      const int qa = qg * Q + q;  // query index within the (sequence, kv head)
+      const int row = seq * rps + qa / HG, head = g * HG + qa % HG;
       st_dev(o + (size_t)row * (p.H * hd) + head * hd + d, A / L);
     }
   }
@@ -1294,9 +1295,9 @@ __device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, in
 // falls in the split, the cache writes and the bf16-rounded copies newk,
 // newv [rps][hd] in LDS (the split's tiles may have been loaded before the
 // rows reached the cache).
-__device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, int l, int seq, int g, int Q,
-                                              int p_lo, int p_hi, const Plan& P, float* Qv, float* newk,
-                                              float* newv, uint16_t* nkb = nullptr, uint16_t* nvb = nullptr) {
+__device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, int l, int seq, int g, int qbase,
+                                              int Q, int p_lo, int p_hi, const Plan& P, float* Qv, uint16_t* nkb,
+                                              uint16_t* nvb, bool write_cache) {
   if (P.U) p_hi = P.F + 1;  // this split also writes the trailing row
   const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
   const int nrows_qkv = (p.H + 2 * p.G) * hd;
@@ -1304,7 +1305,8 @@ __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, 
   const float scale = 1.0f / sqrtf((float)hd);
   for (int it = threadIdx.x; it < Q * (hd / 2); it += kThreads) {
     const int q = it / (hd / 2), i = it % (hd / 2);
-    const int row = seq * rps + q / HG, head = g * HG + q % HG;
+    const int qa = qbase + q;  // query index within the (sequence, kv head)
+    const int row = seq * rps + qa / HG, head = g * HG + qa % HG;
     const float* src = qkv + (size_t)row * nrows_qkv + head * hd;
     const float c = ms->rope[(row * 64 + i) * 2], sn = ms->rope[(row * 64 + i) * 2 + 1];
     const float x0 = src[i], x1 = src[i + hd / 2];
@@ -1324,20 +1326,16 @@ __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, 
     const float x0 = ksrc[i], x1 = ksrc[i + hd / 2];
     const uint16_t k0 = f32_to_bf16(x0 * c - x1 * sn), k1 = f32_to_bf16(x1 * c + x0 * sn);
     const uint16_t v0 = f32_to_bf16(vsrc[i]), v1 = f32_to_bf16(vsrc[i + hd / 2]);
-    kc[(size_t)pos * hd + i] = k0;
-    kc[(size_t)pos * hd + i + hd / 2] = k1;
-    vc[(size_t)pos * hd + i] = v0;
-    vc[(size_t)pos * hd + i + hd / 2] = v1;
-    newk[rr * 128 + i] = __uint_as_float((uint32_t)k0 << 16);
-    newk[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)k1 << 16);
-    newv[rr * 128 + i] = __uint_as_float((uint32_t)v0 << 16);
-    newv[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)v1 << 16);
-    if (nkb) {
-      nkb[rr * 128 + i] = k0;
-      nkb[rr * 128 + i + hd / 2] = k1;
-      nvb[rr * 128 + i] = v0;
-      nvb[rr * 128 + i + hd / 2] = v1;
+    if (write_cache) {  // one query group of the (sequence, kv head) writes the cache
+      kc[(size_t)pos * hd + i] = k0;
+      kc[(size_t)pos * hd + i + hd / 2] = k1;
+      vc[(size_t)pos * hd + i] = v0;
+      vc[(size_t)pos * hd + i + hd / 2] = v1;
     }
+    nkb[rr * 128 + i] = k0;
+    nkb[rr * 128 + i + hd / 2] = k1;
+    nvb[rr * 128 + i] = v0;
+    nvb[rr * 128 + i + hd / 2] = v1;
   }
 }
 
@@ -1367,8 +1365,11 @@ __device__ __forceinline__ float sum_groups(float v) {
 }
 
 // Split-KV GQA decode attention on the matrix cores, for tasks of at most NQ
-// query vectors (sequence rows * heads per kv head).  Task = (sequence, kv
-// head, split) = this CU; the split's positions are spread over the splits
+// query vectors.  The rows * heads-per-kv-head queries of a (sequence, kv
+// head) form q_groups groups of q_per_task (one group for a decode step, two
+// of 16 for 8 verify rows); task = (sequence, kv head, query group, split) =
+// this CU.  The groups of a split read the same tiles; the cached positions
+// are spread over the splits
 // tile by tile and stream as K, V tile pairs of 32 positions.  Wave w owns
 // positions 8w .. 8w+7 of every tile (its 2 KiB quarter, as in a GEMV tile)
 // and takes two pairs (a, b) per step: 16 positions r, r < 8 from a.
@@ -1395,23 +1396,27 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
                                                const Plan& N) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
-  const int Q = rps * HG;
-  const int S = p.n_splits;
-  const int ntask = p.n_seq * p.G * S;
+  const int Q = p.q_per_task;  // query vectors of this task: query group qg of its (sequence, kv head)
+  const int S = p.n_splits, QG = p.q_groups;
+  const int ntask = p.n_seq * p.G * QG * S;
   Misc* ms = sm.misc;
-  float* Qv = sm.xs;                    // [NQ][128]
-  float* newk = Qv + NQ * 128;          // [rps][128]
-  float* newv = newk + kMaxRows * 128;  // [rps][128]
-  float* wst = newv + kMaxRows * 128;   // [kWaves][NQ][kPartStride] wave states; later combine scratch
-  uint16_t* nkb = reinterpret_cast<uint16_t*>(wst + kWaves * NQ * kPartStride);  // [rps][128] bf16 copies
+  // x region: the queries, read into registers before the tile loop, share
+  // their space with the wave states written after it (a workgroup sync
+  // separates the two); the bf16 copies of this step's k, v rows follow.
+  constexpr int kQvF = NQ * 128, kWstF = kWaves * NQ * kPartStride;
+  constexpr int kHeadF = kQvF > kWstF ? kQvF : kWstF;
+  float* Qv = sm.xs;   // [NQ][128]
+  float* wst = sm.xs;  // [kWaves][NQ][kPartStride] wave states; later the combine scratch
+  uint16_t* nkb = reinterpret_cast<uint16_t*>(sm.xs + kHeadF);  // [rps][128] bf16 copies
   uint16_t* nvb = nkb + kMaxRows * 128;
-  static_assert((NQ * 128 + 2 * kMaxRows * 128 + kWaves * NQ * kPartStride) * 4 + 2 * kMaxRows * 128 * 2 <= kXsBytes,
-                "attention scratch exceeds the x region");
+  static_assert(kHeadF * 4 + 2 * kMaxRows * 128 * 2 <= kXsBytes, "attention scratch exceeds the x region");
   const int task = attn_task(p.n_cu);
   const bool active = task < ntask;
-  const int seq = active ? task / (p.G * S) : 0, g = active ? (task / S) % p.G : 0, s = active ? task % S : 0;
+  const int seq = active ? task / (p.G * QG * S) : 0, g = active ? (task / (QG * S)) % p.G : 0;
+  const int qg = active ? (task / S) % QG : 0, s = active ? task % S : 0;
+  const int qbase = qg * Q;
   const int p_lo = P.a0, p_hi = P.a1;
-  if (active) attn_prologue(p, ms, l, seq, g, Q, p_lo, p_hi, P, Qv, newk, newv, nkb, nvb);
+  if (active) attn_prologue(p, ms, l, seq, g, qbase, Q, p_lo, p_hi, P, Qv, nkb, nvb, qg == 0);
   __syncthreads();
   constexpr float kLog2e = 1.4426950408889634f;
   const int qq = lane & 15, lg = lane >> 4;
@@ -1447,7 +1452,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
       }
     }
   }
-  const int rowpos = ms->pos[min(seq * rps + qq / HG, kMaxRows - 1)];
+  const int rowpos = ms->pos[min(seq * rps + (qbase + qq) / HG, kMaxRows - 1)];
   const int qvis = qok ? rowpos : -1;          // last position the lane's query sees
   const int qlim = min(p_hi - 1, qvis);        // ... among the split's tiles
   f32x4_t acc[8];
@@ -1547,6 +1552,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   }
   st.mark(2);
   if (!active) return;
+  __syncthreads();  // every wave has its queries in registers before the wave states overwrite them
   // Wave state: lane l holds query l & 15's sums over dims 16nb + 4(l >> 4)
   // + i; lsum is the lane's share of the query's sum (over 4 lane groups).
   constexpr float kLn2 = 0.6931471805599453f;
@@ -1565,7 +1571,8 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   }
   __syncthreads();
   // merge the 4 wave states into the split partial
-  tagword_t* part = reinterpret_cast<tagword_t*>(act_w(p, l, p.al.part)) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
+  tagword_t* part = reinterpret_cast<tagword_t*>(act_w(p, l, p.al.part)) +
+                    ((size_t)(((seq * p.G + g) * QG + qg) * S + s) * Q) * kPartStride;
   for (int it = threadIdx.x; it < Q * (hd / 4 + 1); it += kThreads) {
     const int q = it / (hd / 4 + 1), k4 = it % (hd / 4 + 1);
     float M = -INFINITY;
@@ -1596,182 +1603,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
     }
   }
   __syncthreads();  // the wave states are read before the gather reuses the x region
-  attn_gather(p, sm, l, seq, g, s, Q);
-}
-
-// Split-KV GQA attention.  Task = (sequence, kv head, split) = this CU.
-// Query vector q = rr*HG + hh is row seq*rps + rr, head g*HG + hh.  Every wave
-// reads every position of a tile; wave w owns the queries q = w, w+4, ...  A
-// lane covers 8 dims (lane & 15) of one position (lane >> 4) per 1 KiB chunk.
-// The split's tiles may have been loaded before this step's rows reached the
-// cache, so the positions written by this step are taken from LDS.
-template <int QW>
-__device__ __forceinline__ void phase_attn(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int HG = p.H / p.G, hd = p.hd, rps = p.rps;
-  const int Q = rps * HG;
-  const int S = p.n_splits;
-  const int ntask = p.n_seq * p.G * S;
-  const int nrows_qkv = (p.H + 2 * p.G) * hd;
-  const float* qkv = act_f(p, l, p.al.qkv);
-  Misc* ms = sm.misc;
-  float* Qv = sm.xs;                          // [Q][hd] queries, RoPE'd and scaled
-  float* newk = sm.xs + kMaxQ * 128;          // [rps][hd] this step's k rows (bf16-rounded)
-  float* newv = newk + kMaxRows * 128;        // [rps][hd]
-  float* coef = newv + kMaxRows * 128;        // [Q][S] combine weights
-  const int task = attn_task(p.n_cu);
-  const bool active = task < ntask;
-  const int seq = active ? task / (p.G * S) : 0, g = active ? (task / S) % p.G : 0, s = active ? task % S : 0;
-  const int p_lo = P.a0, p_hi = P.a1;
-  const float scale = 1.0f / sqrtf((float)hd);
-  const int d0 = (lane & 15) * 8;
-  const int pg = lane >> 4;
-  if (active) {
-    for (int it = threadIdx.x; it < Q * (hd / 2); it += kThreads) {
-      const int q = it / (hd / 2), i = it % (hd / 2);
-      const int row = seq * rps + q / HG, head = g * HG + q % HG;
-      const float* src = qkv + (size_t)row * nrows_qkv + head * hd;
-      const float c = ms->rope[(row * 64 + i) * 2], sn = ms->rope[(row * 64 + i) * 2 + 1];
-      const float x0 = src[i], x1 = src[i + hd / 2];
-      Qv[q * hd + i] = (x0 * c - x1 * sn) * scale;
-      Qv[q * hd + i + hd / 2] = (x1 * c + x0 * sn) * scale;
-    }
-    // this step's rows of the sequence inside the split: RoPE'd bf16 k, bf16 v
-    uint16_t* kc = reinterpret_cast<uint16_t*>(const_cast<char*>(P.b0));
-    uint16_t* vc = reinterpret_cast<uint16_t*>(const_cast<char*>(P.b1));
-    for (int it = threadIdx.x; it < rps * (hd / 2); it += kThreads) {
-      const int rr = it / (hd / 2), i = it % (hd / 2);
-      const int row = seq * rps + rr;
-      const int pos = ms->pos[row];
-      if (pos < p_lo || pos >= p_hi) continue;
-      const float* ksrc = qkv + (size_t)row * nrows_qkv + p.H * hd + g * hd;
-      const float* vsrc = qkv + (size_t)row * nrows_qkv + (p.H + p.G) * hd + g * hd;
-      const float c = ms->rope[(row * 64 + i) * 2], sn = ms->rope[(row * 64 + i) * 2 + 1];
-      const float x0 = ksrc[i], x1 = ksrc[i + hd / 2];
-      const uint16_t k0 = f32_to_bf16(x0 * c - x1 * sn), k1 = f32_to_bf16(x1 * c + x0 * sn);
-      const uint16_t v0 = f32_to_bf16(vsrc[i]), v1 = f32_to_bf16(vsrc[i + hd / 2]);
-      kc[(size_t)pos * hd + i] = k0;
-      kc[(size_t)pos * hd + i + hd / 2] = k1;
-      vc[(size_t)pos * hd + i] = v0;
-      vc[(size_t)pos * hd + i + hd / 2] = v1;
-      newk[rr * 128 + i] = __uint_as_float((uint32_t)k0 << 16);
-      newk[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)k1 << 16);
-      newv[rr * 128 + i] = __uint_as_float((uint32_t)v0 << 16);
-      newv[rr * 128 + i + hd / 2] = __uint_as_float((uint32_t)v1 << 16);
-    }
-  }
-  __syncthreads();
-  // new positions inside this split, per sequence row (-1: none)
-  int newpos[kMaxRows];
-#pragma unroll
-  for (int rr = 0; rr < kMaxRows; ++rr) {
-    newpos[rr] = -1;
-    if (active && rr < rps) {
-      const int pos = ms->pos[seq * rps + rr];
-      if (pos >= p_lo && pos < p_hi) newpos[rr] = pos;
-    }
-  }
-  float qr[QW][8], acc[QW][8], m[QW], lsum[QW], pr[QW][8];
-  int qlim[QW];
-#pragma unroll
-  for (int i = 0; i < QW; ++i) {
-    const int q = wave + 4 * i;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[i][j] = 0.f;
-      pr[i][j] = 0.f;
-      qr[i][j] = (active && q < Q) ? Qv[q * hd + d0 + j] : 0.f;
-    }
-    m[i] = -INFINITY;
-    lsum[i] = 0.f;
-    qlim[i] = (active && q < Q) ? min(p_hi - 1, ms->pos[seq * rps + q / HG]) : -1;  // last visible position
-  }
-  st.mark(1);
-  settle();
-  st.fill<PK_ATTN, PK_WO>(sm, P, N, 0, wave, lane);
-  for (int i = 0; i < P.n; ++i) {
-    st.wait(i);
-    __syncthreads();  // tile i landed for every wave; every wave is done with tile i-1
-    st.fill<PK_ATTN, PK_WO>(sm, P, N, i, wave, lane);
-    const char* slot = st.slot(sm, i);
-    const int t0 = p_lo + (i >> 1) * kAttnTile;
-    const bool is_v = (i & 1) != 0;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int j = t0 + 4 * c + pg;
-      float kf[8];
-      unpack16<uint16_t>(*reinterpret_cast<const uint4*>(slot + c * 1024 + lane * 16), kf);
-#pragma unroll
-      for (int rr = 0; rr < kMaxRows; ++rr) {
-        if (newpos[rr] == j) {
-          const float* src = (is_v ? newv : newk) + rr * 128 + d0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kf[e] = src[e];
-        }
-      }
-      if (!is_v) {
-#pragma unroll
-        for (int i2 = 0; i2 < QW; ++i2) {
-          float dsum = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dsum = fmaf(kf[e], qr[i2][e], dsum);
-          dsum = sum_row16(dsum);
-          pr[i2][c] = (j <= qlim[i2]) ? dsum : -INFINITY;  // scores for now
-        }
-      } else {
-#pragma unroll
-        for (int i2 = 0; i2 < QW; ++i2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i2][e] = fmaf(pr[i2][c], kf[e], acc[i2][e]);
-      }
-    }
-    if (!is_v) {
-      // online softmax over this tile's 32 positions
-#pragma unroll
-      for (int i2 = 0; i2 < QW; ++i2) {
-        float mt = pr[i2][0];
-#pragma unroll
-        for (int c = 1; c < 8; ++c) mt = fmaxf(mt, pr[i2][c]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m[i2], mt);
-        const float corr = (mn == -INFINITY) ? 1.f : __expf(m[i2] - mn);
-        float ps = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          pr[i2][c] = (pr[i2][c] == -INFINITY) ? 0.f : __expf(pr[i2][c] - mn);
-          ps += pr[i2][c];
-        }
-        ps = sum_rows(ps);
-        lsum[i2] = lsum[i2] * corr + ps;
-        m[i2] = mn;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i2][j] *= corr;
-      }
-    }
-  }
-  st.fill<PK_ATTN, PK_WO>(sm, P, N, P.n, wave, lane);
-  st.mark(2);
-  if (!active) return;
-  // sum the 4 position groups; lanes 0-15 hold acc for dims d0..d0+7
-  tagword_t* part = reinterpret_cast<tagword_t*>(act_w(p, l, p.al.part)) + ((size_t)((seq * p.G + g) * S + s) * Q) * kPartStride;
-#pragma unroll
-  for (int i = 0; i < QW; ++i) {
-    const int q = wave + 4 * i;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = sum_rows(acc[i][j]);
-    if (q < Q && lane < 16) {
-      tagword_t* dst = part + (size_t)q * kPartStride;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st_tag(dst + 4 + d0 + j, acc[i][j], p.tag);
-      if (lane == 0) {
-        st_tag(dst + 0, m[i], p.tag);
-        st_tag(dst + 1, lsum[i], p.tag);
-      }
-    }
-  }
-  __syncthreads();  // LDS reads of this task are done before the gather reuses the x region
-  attn_gather(p, sm, l, seq, g, s, Q);
+  attn_gather(p, sm, l, seq, g, qg, s, Q);
 }
 
 // WO: h1 = h + Wo . o
@@ -2297,7 +2129,9 @@ __device__ __forceinline__ void phase_down_b(const KParams& p, Smem sm, int l, i
 
 // ------------------------------------------------------------------ kernel
 
-template <typename WT, int MT, int QW>
+// WT: weight element type; MT: rows of the token group (1 or 8); QK: kind of
+// attention task, 1: at most 4 query vectors, 2: at most 16
+template <typename WT, int MT, int QK>
 __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   Smem sm;
   sm.ring = smem_raw;
@@ -2359,7 +2193,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   for (int l = 0; l < p.L; ++l) {
     if (p.attn) {
       {
-        const Plan nxt = plan_attn(p, ms, l, QW == 1);
+        const Plan nxt = plan_attn(p, ms, l, true);
         phase_qkv<WT, MT>(p, sm, l, st, cur, nxt);
         MK_SYNC();
         st.advance(cur);
@@ -2367,8 +2201,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
       }
       {
         const Plan nxt = plan_wo<WT>(p, l);
-        if constexpr (QW == 1) phase_attn_dec<4>(p, sm, l, st, cur, nxt);
-        else phase_attn<QW>(p, sm, l, st, cur, nxt);
+        phase_attn_dec<QK == 1 ? 4 : 16>(p, sm, l, st, cur, nxt);
         MK_SYNC();
         st.advance(cur);
         cur = nxt;
@@ -2428,12 +2261,12 @@ extern "C" int mk_launch_kernel(const mk::KParams* pp, void* stream) {
   KParams p = *pp;
   const size_t lds = (size_t)kLdsTotal;
   if (p.M > kMaxRows) return -2;
-  if (p.attn && p.n_seq * p.G * p.n_splits > p.n_cu) return -2;
+  if (p.attn && p.n_seq * p.G * p.q_groups * p.n_splits > p.n_cu) return -2;
   const int Q = p.attn ? p.q_per_task : 0;
   const void* fn;
   int idx;
-  // instantiations: weight dtype x token group (1 or 8) x attention kind
-  // (1: decode attention, at most 4 query vectors per task; 8: up to 32)
+  // instantiations: weight dtype x token group (1 or 8) x attention task
+  // kind (1: at most 4 query vectors, decode; 2: at most 16, verify)
   if (p.wide) {
     if (Q > 4) return -2;
     fn = p.M == 1 ? (const void*)decode_step_kernel<float, 1, 1> : (const void*)decode_step_kernel<float, 8, 1>;
@@ -2442,8 +2275,8 @@ extern "C" int mk_launch_kernel(const mk::KParams* pp, void* stream) {
     fn = p.M == 1 ? (const void*)decode_step_kernel<uint16_t, 1, 1> : (const void*)decode_step_kernel<uint16_t, 8, 1>;
     idx = p.M == 1 ? 2 : 3;
   } else {
-    if (Q > 4 * 8) return -2;
-    fn = (const void*)decode_step_kernel<uint16_t, 8, 8>;
+    if (Q > 16) return -2;
+    fn = (const void*)decode_step_kernel<uint16_t, 8, 2>;
     idx = 4;
   }
   static bool attr_done[5] = {false, false, false, false, false};

@@ -50,6 +50,8 @@ struct mk_handle {
   int device;
   int n_cu;
   int n_splits;
+  int q_groups;  // attention tasks per (sequence, kv head, split)
+  int q_task;    // query vectors per attention task
   int barriers;
   int ring_tiles;
   int x_bytes;
@@ -172,16 +174,28 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   const int n_seq = M / c.rows_per_seq;
   const int H = c.has_attn ? c.n_heads : 0, G = c.has_attn ? c.n_kv_heads : 0, hd = c.has_attn ? c.head_dim : 0;
   h->n_splits = 1;
+  h->q_groups = 1;
+  h->q_task = 0;
   if (c.has_attn) {
-    int s = h->n_cu / (n_seq * G);
+    // Up to 4 query vectors share a task (decode); more (several rows of a
+    // sequence: verify) are split into groups of at most 16, one MFMA
+    // operand each, which read the same cache tiles.
+    const int Qall = c.rows_per_seq * (c.n_heads / c.n_kv_heads);
+    h->q_groups = Qall <= 4 ? 1 : (Qall + mk::kMaxQTask - 1) / mk::kMaxQTask;
+    if (Qall % h->q_groups) {
+      delete h;
+      return fail(MK_ERR_UNSUPPORTED, "rows_per_seq * n_heads / n_kv_heads = %d does not split into equal query "
+                  "groups of at most %d", Qall, mk::kMaxQTask);
+    }
+    h->q_task = Qall / h->q_groups;
+    int s = h->n_cu / (n_seq * G * h->q_groups);
     if (s < 1) s = 1;
     int maxs = (c.kv_capacity + mk::kAttnTile - 1) / mk::kAttnTile;
     if (s > maxs) s = maxs;
     h->n_splits = s;
     // the split combine gathers, per split, the (m, l) words of the queries
     // its output slice touches and the slice's acc words into the x region
-    const int Q = c.rows_per_seq * (c.n_heads / c.n_kv_heads);
-    const int nout = Q * hd, nper = (nout + s - 1) / s;
+    const int nout = h->q_task * hd, nper = (nout + s - 1) / s;
     int maxw = 0;
     for (int z = 0; z < s; ++z) {
       const int o0 = z * nper, o1 = std::min(o0 + nper, nout);
@@ -338,7 +352,8 @@ int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* position
     p.wide = c.dtype == MK_F32 ? 1 : 0;
     p.eps = c.rms_eps; p.theta = c.rope_theta;
     p.n_splits = h->n_splits;
-    p.q_per_task = c.has_attn ? c.rows_per_seq * (c.n_heads / c.n_kv_heads) : 0;
+    p.q_per_task = h->q_task;
+    p.q_groups = h->q_groups;
     p.n_cu = h->n_cu;
     p.ring_tiles = h->ring_tiles;
     p.x_bytes = h->x_bytes;
