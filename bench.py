@@ -17,6 +17,11 @@ kernel's average duration from HIP events on its stream, against 8 TB/s.
 cpu_baseline: the CPU oracle timed on a bounded sample of layers of the same
 step, scaled to tokens/s.
 
+Other legs, reported beside the headline: batch 8 over the same weights; the
+verify pass (1 and 8 sequences x 8 rows); speculative decoding around the
+verify pass with a synthetic acceptance process (effective tokens/s at about
+6 tokens per step); the 16-layer MoE-only stack at batch 1 and 8.
+
 HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
 this script with --calib-copy-mib, one with --pmc FETCH_SIZE and one with
 --pmc WRITE_SIZE; `python bench.py --parse-pmc FETCH_DIR WRITE_DIR` reads
@@ -125,6 +130,55 @@ def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush
                 achieved_gbps=gbps, frac=gbps / PEAK_HBM_GBPS,
                 union_mean=float(np.mean([np.mean(u) for u in unions[warmup:]])), barriers=info.barriers_per_step,
                 finite=finite, union_per_layer=union_layers if trace_union else None)
+
+
+def spec_leg(torch, mk, st, w, n_seq, steps, warmup, alpha=0.9155, seed=5):
+    """Speculative decoding around the verify step, with a synthetic acceptance
+    process: each step runs 8 rows per sequence (the last accepted token and
+    7 drafts) at positions p .. p+7; each draft is accepted with probability
+    alpha until the first rejection, so a step yields 1 + a tokens (a <= 7,
+    mean 6.0 at alpha 0.9155) and the sequence continues at p + 1 + a.  The
+    rejected drafts' cache entries are overwritten by the next step's rows
+    before they could be read, which is the rollback.  effective tok/s =
+    tokens yielded / time of the timed steps (HIP events around each launch)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    M = 8 * n_seq
+    cfg = st.config(rows=M, rows_per_seq=8)
+    h = mk.mk_create(cfg, st.layer_weights())
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    bufs = [st.hidden(100 + i, rows=M) for i in range(2)]
+    out = torch.empty(M, w.d, dtype=torch.float32, device="cuda")
+    kv = st.kv()
+    p = np.full(n_seq, w.past, dtype=np.int64)
+    ev, toks = [], []
+    for t in range(warmup + steps):
+        pos = np.array([p[s] + r for s in range(n_seq) for r in range(8)], dtype=np.int32)
+        if pos.max() >= w.capacity:
+            raise SystemExit("spec leg: KV capacity too small for the steps asked")
+        pos_d = torch.as_tensor(pos, device="cuda")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        mk.mk_decode_step(h, bufs[t % 2].data_ptr(), pos_d.data_ptr(), kv, out.data_ptr(), sp)
+        b.record(stream)
+        acc = np.zeros(n_seq, dtype=np.int64)
+        for s in range(n_seq):
+            while acc[s] < 7 and rng.random() < alpha:
+                acc[s] += 1
+        p += 1 + acc
+        if t >= warmup:
+            ev.append((a, b))
+            toks.append(int((1 + acc).sum()))
+    torch.cuda.synchronize()
+    rc = mk.mk_sync(h, sp)
+    mk.mk_destroy(h)
+    if rc != mk.MK_OK:
+        raise mk.MkError(rc, mk.mk_last_error())
+    ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    return dict(sequences=n_seq, rows=M, ms_per_step=ms, tokens_per_step=float(np.mean(toks)) / n_seq,
+                effective_tok_s=float(np.sum(toks)) / (ms * 1e-3 * len(ev)), accept_alpha=alpha,
+                finite=bool(torch.isfinite(out).all().item()))
 
 
 def moe16_legs(torch, mk, steps, warmup):
@@ -242,7 +296,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-verify", action="store_true", help="skip the 8- and 64-row verify legs")
+    ap.add_argument("--no-verify", action="store_true", help="skip the 8- and 64-row verify and speculative legs")
     ap.add_argument("--no-moe16", action="store_true", help="skip the 16-layer MoE-only legs")
     ap.add_argument("--moe16-steps", type=int, default=256, help="timed steps of the 16-layer legs")
     ap.add_argument("--cpu-layers", type=int, default=92, help="layers in the CPU-oracle sample (default: a whole step)")
@@ -274,7 +328,7 @@ def main():
         synth.build()
     need = args.warmup + args.steps
     n_seq = 1 if args.no_batch8 else 8
-    w8 = ATTN92_B8.with_(cap_extra=max(64, need + 8), M=n_seq)
+    w8 = ATTN92_B8.with_(cap_extra=max(64, 8 * (need + 2)), M=n_seq)  # room for 8 positions per spec step
     t0 = time.perf_counter()
     def prog(l):
         if l % 16 == 0:
@@ -303,6 +357,12 @@ def main():
                 f"{v['achieved_gbps']:.0f} GB/s algorithmic ({100 * v['frac']:.1f}% of peak), union {v['union_mean']:.1f}")
             v["rows_s"] = v.pop("tok_s")
             verify[f"verify{M}"] = {k: (round(x, 4) if isinstance(x, float) else x) for k, x in v.items()}
+        for n_sp in ((1, 8) if st.w.n_seq >= 8 else (1,)):
+            sp_steps = args.steps if n_sp == 1 else min(args.steps, 10)
+            r = spec_leg(torch, mk, st, w8, n_sp, sp_steps, 1)
+            log(f"speculative, {n_sp} sequence(s) x 8 rows: {r['ms_per_step']:.3f} ms/step, "
+                f"{r['tokens_per_step']:.2f} tokens per sequence and step, {r['effective_tok_s']:.1f} effective tok/s")
+            verify[f"spec{8 * n_sp}"] = {k: (round(x, 4) if isinstance(x, float) else x) for k, x in r.items()}
     moe16 = {}
     if not args.no_moe16:
         moe16 = moe16_legs(torch, mk, args.moe16_steps, args.warmup)

@@ -1,0 +1,69 @@
+"""Speculative decoding around the verify step: rollback of rejected drafts.
+
+A verify step writes the K/V rows of all 8 of its rows (the last accepted
+token and 7 drafts) before attending.  When only the first a drafts are
+accepted, the next step starts at position p + a + 1 and its rows overwrite
+the rejected drafts' cache entries before anything reads them.  So nothing of
+a rejected draft may reach a later step: the step after a rejection must give
+the same bits whether the rejected positions hold the drafts or anything
+else, and it must match the oracle walked over the cache as it stands.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_layer_stack_amd as mk
+    mk.lib()
+    return torch
+
+
+def test_rejected_drafts_do_not_reach_the_next_step(env):
+    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+    from synth.stack import DeviceStack
+    from synth.workloads import VERIFY92_M8
+    torch = env
+    w = VERIFY92_M8
+    st = DeviceStack(w, n_layers=2)
+    run = GpuRun(st)
+    try:
+        p0 = w.past
+        accepted = 2  # drafts accepted in step 1: tokens p0 .. p0+2 stay, p0+3 .. p0+7 are rolled back
+        p1 = p0 + accepted + 1
+        pristine = [(st.kc[l, 0].clone(), st.vc[l, 0].clone()) for l in range(st.L)]
+        _say(f"{w.name} L=2 step 1 at {p0}..{p0 + 7}")
+        run.step(st.hidden(0), [p0 + r for r in range(8)])
+        after1 = [(st.kc[l, 0].clone(), st.vc[l, 0].clone()) for l in range(st.L)]
+        kv_hosts = [st.host_kv(l) for l in range(st.L)]
+        pos2 = [p1 + r for r in range(8)]
+        hid2 = st.hidden(1)
+        _say(f"{w.name} step 2 at {p1}..{p1 + 7} over the rejected drafts")
+        out_a = run.step(hid2, pos2).clone()
+        ids_a, _, _ = run.trace()
+        # the same step over a cache whose rejected positions never held the drafts
+        for l in range(st.L):
+            st.kc[l, 0].copy_(after1[l][0])
+            st.vc[l, 0].copy_(after1[l][1])
+            st.kc[l, 0, :, p1:p0 + 8].copy_(pristine[l][0][:, p1:p0 + 8])
+            st.vc[l, 0, :, p1:p0 + 8].copy_(pristine[l][1][:, p1:p0 + 8])
+        torch.cuda.synchronize()
+        _say(f"{w.name} step 2 again with positions {p1}..{p0 + 7} restored")
+        out_b = run.step(hid2, pos2).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), "a rejected draft reached the next step"
+        ref, rep = oracle_walk(st, hid2.cpu().numpy(), pos2, ids_a, rows_per_seq=8, kv_hosts=kv_hosts)
+        assert not rep["mismatch"], rep["mismatch"][:5]
+        c = assert_close(out_a.cpu().numpy(), ref, tolerances(w), "step after rollback")
+        _say(f"{w.name} rollback ok {c}")
+    finally:
+        run.close()
