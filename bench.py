@@ -20,7 +20,9 @@ step, scaled to tokens/s.
 Other legs, reported beside the headline: batch 8 over the same weights; the
 verify pass (1 and 8 sequences x 8 rows); speculative decoding around the
 verify pass with a synthetic acceptance process (effective tokens/s at about
-6 tokens per step); the 16-layer MoE-only stack at batch 1 and 8.
+6 tokens per step); the same step as one kernel launch per phase of every
+layer (the many-kernels baseline, batch 1 and 8); the 16-layer MoE-only
+stack at batch 1 and 8.
 
 HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
 this script with --calib-copy-mib, one with --pmc FETCH_SIZE and one with
@@ -71,12 +73,14 @@ def step_bytes(w, M, n_seq, union_per_layer, kv_read_positions):
     return total
 
 
-def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush=None):
+def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush=None, phased=False):
     """Time `steps` decode steps of batch M (after `warmup`).  Returns dict.
 
     flush: (src, dst) device buffers; when given, dst.copy_(src) runs on the
     stream before every launch, outside the events that time the launch, so
-    each step starts with nothing of the stack in the Infinity Cache or L2."""
+    each step starts with nothing of the stack in the Infinity Cache or L2.
+    phased: run the step as one launch per phase of every layer
+    (mk_decode_step_phased) instead of the persistent kernel."""
     import numpy as np
     cfg = st.config(rows=M, rows_per_seq=rows_per_seq)
     h = mk.mk_create(cfg, st.layer_weights())
@@ -104,7 +108,8 @@ def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush
             flush[1].copy_(flush[0])
         if timed:
             ev[t - warmup][0].record(stream)
-        mk.mk_decode_step(h, bufs[t % 2].data_ptr(), pos_d[t].data_ptr(), kv, bufs[(t + 1) % 2].data_ptr(), sp)
+        step_fn = mk.mk_decode_step_phased if phased else mk.mk_decode_step
+        step_fn(h, bufs[t % 2].data_ptr(), pos_d[t].data_ptr(), kv, bufs[(t + 1) % 2].data_ptr(), sp)
         if timed:
             ev[t - warmup][1].record(stream)
     torch.cuda.synchronize()
@@ -125,11 +130,13 @@ def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush
     gbps = float(np.mean(byts)) / (ms * 1e-3) / 1e9
     finite = bool(torch.isfinite(bufs[total % 2]).all().item())
     union_layers = [round(float(np.mean([unions[t][l] for t in range(warmup, total)])), 2) for l in range(st.L)]
+    n_groups = max(1, M // 8)
+    launches = n_groups * (st.L * ((6 if w.has_attn else 3) + (1 if M > 1 else 0)) if phased else 1)
     return dict(M=M, ms_per_step=ms, ms_p10=float(np.percentile(durs, 10)), ms_p90=float(np.percentile(durs, 90)),
                 wall_ms_per_step=t_wall * 1e3 / steps, tok_s=M / (ms * 1e-3), bytes_per_step=float(np.mean(byts)),
                 achieved_gbps=gbps, frac=gbps / PEAK_HBM_GBPS,
                 union_mean=float(np.mean([np.mean(u) for u in unions[warmup:]])), barriers=info.barriers_per_step,
-                finite=finite, union_per_layer=union_layers if trace_union else None)
+                finite=finite, union_per_layer=union_layers if trace_union else None, launches=launches)
 
 
 def spec_leg(torch, mk, st, w, n_seq, steps, warmup, alpha=0.9155, seed=5):
@@ -298,6 +305,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="skip the 8- and 64-row verify and speculative legs")
     ap.add_argument("--no-moe16", action="store_true", help="skip the 16-layer MoE-only legs")
+    ap.add_argument("--no-phased", action="store_true", help="skip the one-launch-per-phase baseline legs")
     ap.add_argument("--moe16-steps", type=int, default=256, help="timed steps of the 16-layer legs")
     ap.add_argument("--cpu-layers", type=int, default=92, help="layers in the CPU-oracle sample (default: a whole step)")
     ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the workload's 92)")
@@ -363,6 +371,20 @@ def main():
             log(f"speculative, {n_sp} sequence(s) x 8 rows: {r['ms_per_step']:.3f} ms/step, "
                 f"{r['tokens_per_step']:.2f} tokens per sequence and step, {r['effective_tok_s']:.1f} effective tok/s")
             verify[f"spec{8 * n_sp}"] = {k: (round(x, 4) if isinstance(x, float) else x) for k, x in r.items()}
+    phased = {}
+    if not args.no_phased:
+        # the same step as one kernel launch per phase of every layer: the
+        # many-kernels execution the persistent kernel replaces
+        for name, M, wl in (("phased_b1", 1, w1), ("phased_b8", 8, w8)):
+            if M > st.w.n_seq:
+                continue
+            r = run_leg(torch, mk, st, wl, M, 1, min(args.steps, 10), 2, trace_union=False, phased=True)
+            ref = b1 if M == 1 else b8
+            r["persistent_ms_per_step"] = ref["ms_per_step"] if ref else None
+            log(f"{name}: {r['ms_per_step']:.3f} ms/step as {r['launches']} launches, {r['tok_s']:.1f} tok/s "
+                f"({100 * r['frac']:.1f}% of peak); the persistent kernel: "
+                f"{ref['ms_per_step'] if ref else float('nan'):.3f} ms/step")
+            phased[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
     moe16 = {}
     if not args.no_moe16:
         moe16 = moe16_legs(torch, mk, args.moe16_steps, args.warmup)
@@ -414,6 +436,7 @@ def main():
         "batch8": None if b8 is None else {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b8.items()},
     }
     out.update(verify)
+    out.update(phased)
     out.update(moe16)
     print(json.dumps(out), flush=True)
 

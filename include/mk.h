@@ -155,6 +155,18 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
 int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
                    float* hidden_out, void* stream);
 
+/* The same step as a sequence of kernel launches, one per phase of every
+ * layer (QKV, attention, output projection, router + shared gate/up, routed
+ * gate/up, down projection; 6 per layer, 7 with several rows), with no
+ * weight prefetch across a launch boundary.  This is the many-small-kernels
+ * execution that P4 (the paragraph on kernel-boundary bubbles) measures the
+ * megakernel against, kept as a baseline.  It runs the same phase code, so
+ * hidden_out, the cache rows and the trace equal those of mk_decode_step
+ * bit for bit.  Arguments, ownership and errors as mk_decode_step;
+ * mk_set_timing does not apply. */
+int mk_decode_step_phased(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+                          float* hidden_out, void* stream);
+
 /* Free the workspace and the handle.  NULL is accepted. */
 int mk_destroy(mk_handle* h);
 

@@ -31,6 +31,10 @@ constexpr int kResFloats = kPartBytes / 4 - kPartAcc;  // epilogue residual slic
 // device error flag bits
 enum : unsigned { kErrTimeout = 1u, kErrPosition = 2u, kErrDupPosition = 4u };
 
+// phases of a layer, in order (attention stacks run all; MoE-only stacks
+// start at PH_RS; PH_DOWNB only with several rows)
+enum Phase : int { PH_QKV = 0, PH_ATTN, PH_WO, PH_RS, PH_RG, PH_DOWN, PH_DOWNB };
+
 // Device copy of one layer's weight pointers.
 struct DevLayer {
   const void* attn_norm;
@@ -87,6 +91,7 @@ struct KParams {
   int n_splits;              // KV splits per (seq, kv head)
   int q_per_task;            // query vectors per attention task: rps * (H / G) / q_groups
   int q_groups;              // attention tasks per (seq, kv head, split), each with its own queries
+  int only_l, only_ph;       // one phase per launch: its layer and Phase; only_ph < 0: the whole step
   // launch geometry / LDS carve-up
   int n_cu;
   int ring_tiles;

@@ -215,9 +215,14 @@ extern __shared__ __attribute__((aligned(16))) char smem_raw[];
 // every group's release flag, which the group's workgroups poll.  Counters
 // only grow (targets are epoch + barrier index), so nothing is reset between
 // launches.  A poll that exceeds the watchdog sets the error flag and every
-// workgroup leaves the kernel at its next barrier.  Ring loads issued before
-// the barrier stay in flight through it.
+// workgroup leaves the kernel at its next barrier.  Cross-CU data is written
+// with device-scope stores to write-once locations, and every wave waits for
+// its stores before the arrival; readers use plain loads after the barrier.
 __device__ __forceinline__ bool grid_sync(const KParams& p, Smem sm, unsigned target) {
+  // Release: every wave's device-scope stores of the phase have completed
+  // before the arrival can be seen.  Vector memory has one counter on this
+  // chip, so this also waits for the ring loads the wave has in flight.
+  wait_all();
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned* s = p.sync;
@@ -2129,19 +2134,22 @@ __device__ __forceinline__ void phase_down_b(const KParams& p, Smem sm, int l, i
 
 // ------------------------------------------------------------------ kernel
 
-// WT: weight element type; MT: rows of the token group (1 or 8); QK: kind of
-// attention task, 1: at most 4 query vectors, 2: at most 16
-template <typename WT, int MT, int QK>
-__global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
+// LDS carve-up of the kernels
+__device__ __forceinline__ Smem smem_carve() {
   Smem sm;
   sm.ring = smem_raw;
   sm.xs = reinterpret_cast<float*>(smem_raw + (size_t)kRing * kSlotBytes);
   sm.part = reinterpret_cast<float*>(smem_raw + (size_t)kRing * kSlotBytes + kXsBytes);
   sm.misc = reinterpret_cast<Misc*>(smem_raw + (size_t)kRing * kSlotBytes + kXsBytes + kPartBytes);
+  return sm;
+}
+
+// Launch set-up: positions (range and distinctness within a sequence; every
+// CU checks the same data, so all leave together on a bad input, which
+// block 0 reports on the error flag), the launch's barrier epoch and the
+// RoPE table.  Returns false when the launch must end.
+__device__ __forceinline__ bool launch_setup(const KParams& p, Smem sm) {
   Misc* ms = sm.misc;
-  const KParams& p = kp;
-  // positions: range and distinctness within a sequence (every CU checks the
-  // same data, so all leave together on a bad input)
   if (threadIdx.x == 0) {
     int bad = 0;
     for (int r = 0; r < p.M; ++r) {
@@ -2160,7 +2168,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   if (ms->flag) {
     if (blockIdx.x == 0 && threadIdx.x == 0)
       __hip_atomic_fetch_or(p.sync + SyncLayout::kErr, (unsigned)ms->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
+    return false;
   }
   if (p.attn) {
     // RoPE table: angle = pos * theta^(-2i/hd), evaluated in double, rounded to fp32
@@ -2172,6 +2180,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
       ms->rope[(r * 64 + i) * 2 + 1] = (float)sin(a);
     }
   }
+  return true;
+}
+
+// WT: weight element type; MT: rows of the token group (1 or 8); QK: kind of
+// attention task, 1: at most 4 query vectors, 2: at most 16
+template <typename WT, int MT, int QK>
+__global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
+  const Smem sm = smem_carve();
+  Misc* ms = sm.misc;
+  const KParams& p = kp;
+  if (!launch_setup(p, sm)) return;
   const unsigned epoch0 = (unsigned)ms->epoch;
   __syncthreads();
   unsigned b = 0;
@@ -2254,32 +2273,106 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u(p.sync + SyncLayout::kEpoch, epoch0 + b);
 }
 
+// One phase of one layer per launch: the same phase code as the persistent
+// kernel, with an empty ring at the start and no next phase to prefetch.
+// The state a phase inherits inside the persistent kernel is rebuilt from
+// the workspace: the normed x registers of the MoE block (RG), the routing
+// tables (recomputed from the stored logits; deterministic) and the
+// residual slice of the second DOWN half.  The kernel boundary replaces the
+// grid barrier.  This is the many-kernels baseline the persistent kernel is
+// measured against.
+template <typename WT, int MT, int QK>
+__global__ void __launch_bounds__(kThreads, 1) phase_step_kernel(KParams kp) {
+  const Smem sm = smem_carve();
+  Misc* ms = sm.misc;
+  const KParams& p = kp;
+  if (!launch_setup(p, sm)) return;
+  __syncthreads();
+  const int l = p.only_l;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const Plan none{};
+  Stream st{0, 0, nullptr, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring)};
+  XRegs<WT, MT> xr;
+  switch (p.only_ph) {
+    case PH_QKV:
+      phase_qkv<WT, MT>(p, sm, l, st, plan_qkv<WT>(p, l), none);
+      break;
+    case PH_ATTN:
+      phase_attn_dec<QK == 1 ? 4 : 16>(p, sm, l, st, plan_attn(p, ms, l, true), none);
+      break;
+    case PH_WO:
+      phase_wo<WT, MT>(p, sm, l, st, plan_wo<WT>(p, l), none);
+      break;
+    case PH_RS:
+      phase_rs<WT, MT>(p, sm, l, st, plan_rs<WT>(p, l), none, xr);
+      break;
+    case PH_RG: {
+      load_x_norm<WT, MT>(xr, sm, layer_h1(p, l), p.d, reinterpret_cast<const WT*>(layer_tab(p)[l].moe_norm), p.M,
+                          p.d, p.eps, wave, lane, plan_rs<WT>(p, l).lrb);
+      rg_stage(p, sm, l);
+      route_topk(p, sm, l);
+      phase_rg<WT, MT>(p, sm, l, st, plan_rg<WT>(p, ms, l, true), none, xr);
+      break;
+    }
+    case PH_DOWN:
+      route_topk(p, sm, l);
+      if constexpr (MT == 1) phase_down<WT, MT>(p, sm, l, st, plan_down<WT>(p, ms, l), none);
+      else phase_down_a<WT, MT>(p, sm, l, st, plan_down_a<WT>(p, ms, l), none);
+      break;
+    case PH_DOWNB: {
+      route_topk(p, sm, l);
+      const Plan P = plan_down_a<WT>(p, ms, l);
+      const int c0 = P.lo2 * P.rpt, ncol = P.n1 * P.rpt;
+      load_res(sm, layer_h1(p, l), p.S > 0 ? act_f(p, l, p.al.y_s) : nullptr, p.d, c0, ncol, p.M);
+      __syncthreads();
+      phase_down_b(p, sm, l, c0, ncol);
+      break;
+    }
+    default:
+      break;
+  }
+  wait_all();
+}
+
 }  // namespace mk
+
+// kernel of (weight dtype, token group, attention task kind) for a launch
+static int mk_pick(const mk::KParams& p, bool phased, const void** fn, int* idx) {
+  using namespace mk;
+  if (p.M > kMaxRows) return -2;
+  if (p.attn && p.n_seq * p.G * p.q_groups * p.n_splits > p.n_cu) return -2;
+  const int Q = p.attn ? p.q_per_task : 0;
+  // instantiations: weight dtype x token group (1 or 8) x attention task
+  // kind (1: at most 4 query vectors, decode; 2: at most 16, verify)
+  if (p.wide) {
+    if (Q > 4) return -2;
+    if (phased) *fn = p.M == 1 ? (const void*)phase_step_kernel<float, 1, 1> : (const void*)phase_step_kernel<float, 8, 1>;
+    else *fn = p.M == 1 ? (const void*)decode_step_kernel<float, 1, 1> : (const void*)decode_step_kernel<float, 8, 1>;
+    *idx = p.M == 1 ? 0 : 1;
+  } else if (Q <= 4) {
+    if (phased)
+      *fn = p.M == 1 ? (const void*)phase_step_kernel<uint16_t, 1, 1> : (const void*)phase_step_kernel<uint16_t, 8, 1>;
+    else
+      *fn = p.M == 1 ? (const void*)decode_step_kernel<uint16_t, 1, 1> : (const void*)decode_step_kernel<uint16_t, 8, 1>;
+    *idx = p.M == 1 ? 2 : 3;
+  } else {
+    if (Q > 16) return -2;
+    *fn = phased ? (const void*)phase_step_kernel<uint16_t, 8, 2> : (const void*)decode_step_kernel<uint16_t, 8, 2>;
+    *idx = 4;
+  }
+  if (phased) *idx += 5;
+  return 0;
+}
 
 extern "C" int mk_launch_kernel(const mk::KParams* pp, void* stream) {
   using namespace mk;
   KParams p = *pp;
   const size_t lds = (size_t)kLdsTotal;
-  if (p.M > kMaxRows) return -2;
-  if (p.attn && p.n_seq * p.G * p.q_groups * p.n_splits > p.n_cu) return -2;
-  const int Q = p.attn ? p.q_per_task : 0;
-  const void* fn;
-  int idx;
-  // instantiations: weight dtype x token group (1 or 8) x attention task
-  // kind (1: at most 4 query vectors, decode; 2: at most 16, verify)
-  if (p.wide) {
-    if (Q > 4) return -2;
-    fn = p.M == 1 ? (const void*)decode_step_kernel<float, 1, 1> : (const void*)decode_step_kernel<float, 8, 1>;
-    idx = p.M == 1 ? 0 : 1;
-  } else if (Q <= 4) {
-    fn = p.M == 1 ? (const void*)decode_step_kernel<uint16_t, 1, 1> : (const void*)decode_step_kernel<uint16_t, 8, 1>;
-    idx = p.M == 1 ? 2 : 3;
-  } else {
-    if (Q > 16) return -2;
-    fn = (const void*)decode_step_kernel<uint16_t, 8, 2>;
-    idx = 4;
-  }
-  static bool attr_done[5] = {false, false, false, false, false};
+  const void* fn = nullptr;
+  int idx = 0;
+  const int pk = mk_pick(p, p.only_ph >= 0, &fn, &idx);
+  if (pk != 0) return pk;
+  static bool attr_done[10] = {false, false, false, false, false, false, false, false, false, false};
   if (!attr_done[idx]) {
     // the kernel takes all of the CU's LDS dynamically: any static LDS (a
     // library routine that declares its own) would make the launch fail

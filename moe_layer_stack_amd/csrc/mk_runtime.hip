@@ -318,8 +318,21 @@ int mk_get_info(const mk_handle* h, mk_info* info) {
   return MK_OK;
 }
 
-int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
-                   float* hidden_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int launch_status(int e) {
+  if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
+  if (e == -3) return fail(MK_ERR_HIP, "the kernel declares static LDS, which leaves no room for its ring");
+  if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  return MK_OK;
+}
+
+// One step: per group of up to kMaxRows rows, either one launch of the
+// persistent kernel or (phased) one launch per phase of every layer.
+int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+             float* hidden_out, void* stream, bool phased) {
   if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
   if (!hidden_in || !hidden_out || !positions) return fail(MK_ERR_INVALID_ARG, "NULL device pointer");
   const mk_config& c = h->cfg;
@@ -371,13 +384,41 @@ int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* position
     if (++h->launch_tag == 0) h->launch_tag = 1;
     p.tag = h->launch_tag;
     p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
-    p.stamps = reinterpret_cast<long long*>(h->stamps);
-    int e = mk_launch_kernel(&p, stream);
-    if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
-    if (e == -3) return fail(MK_ERR_HIP, "the kernel declares static LDS, which leaves no room for its ring");
-    if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));
+    if (!phased) {
+      p.stamps = reinterpret_cast<long long*>(h->stamps);
+      p.only_l = 0;
+      p.only_ph = -1;
+      const int st = launch_status(mk_launch_kernel(&p, stream));
+      if (st != MK_OK) return st;
+      continue;
+    }
+    p.stamps = nullptr;
+    const int ph0 = c.has_attn ? mk::PH_QKV : mk::PH_RS;
+    const int ph1 = Mg > 1 ? mk::PH_DOWNB : mk::PH_DOWN;
+    for (int l = 0; l < c.n_layers; ++l) {
+      for (int ph = ph0; ph <= ph1; ++ph) {
+        p.only_l = l;
+        p.only_ph = ph;
+        const int st = launch_status(mk_launch_kernel(&p, stream));
+        if (st != MK_OK) return st;
+      }
+    }
   }
   return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+                   float* hidden_out, void* stream) {
+  return run_step(h, hidden_in, positions, kv, hidden_out, stream, false);
+}
+
+int mk_decode_step_phased(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+                          float* hidden_out, void* stream) {
+  return run_step(h, hidden_in, positions, kv, hidden_out, stream, true);
 }
 
 int mk_sync(mk_handle* h, void* stream) {
