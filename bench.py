@@ -378,7 +378,8 @@ def main():
         for name, M, wl in (("phased_b1", 1, w1), ("phased_b8", 8, w8)):
             if M > st.w.n_seq:
                 continue
-            r = run_leg(torch, mk, st, wl, M, 1, min(args.steps, 10), 2, trace_union=False, phased=True)
+            r = run_leg(torch, mk, st, wl, M, 1, min(args.steps, 10), 2, trace_union=M > 1, phased=True)
+            r.pop("union_per_layer", None)
             ref = b1 if M == 1 else b8
             r["persistent_ms_per_step"] = ref["ms_per_step"] if ref else None
             log(f"{name}: {r['ms_per_step']:.3f} ms/step as {r['launches']} launches, {r['tok_s']:.1f} tok/s "
