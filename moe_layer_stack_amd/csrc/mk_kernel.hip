@@ -1295,11 +1295,12 @@ __device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, in
   }
 }
 
-// Queries of a task, their rotary embedding and this step's new k, v rows:
-// Qv[q][hd] (RoPE'd, scaled by 1/sqrt(hd)) and, for the rows whose position
-// falls in the split, the cache writes and the bf16-rounded copies newk,
-// newv [rps][hd] in LDS (the split's tiles may have been loaded before the
-// rows reached the cache).
+// Queries of a task (query group qbase / Q of its sequence and kv head),
+// their rotary embedding and this step's new k, v rows: Qv[q][hd] (RoPE'd,
+// scaled by 1/sqrt(hd)) and, for the rows whose position falls in the split,
+// the bf16-rounded copies nkb, nvb [rps][hd] in LDS (the split's tiles may
+// have been loaded before the rows reached the cache) and, when write_cache,
+// the cache writes.
 __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, int l, int seq, int g, int qbase,
                                               int Q, int p_lo, int p_hi, const Plan& P, float* Qv, uint16_t* nkb,
                                               uint16_t* nvb, bool write_cache) {

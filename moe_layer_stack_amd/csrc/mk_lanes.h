@@ -36,15 +36,6 @@ __device__ __forceinline__ float sum_rows(float v) {
   const float t = swap16_sum(v, v);
   return swap32_sum(t, t);
 }
-// sum over the 16 lanes of each row, in every lane of the row
-__device__ __forceinline__ float sum_row16(float v) {
-  v += dpp<kDppXor1>(v);
-  v += dpp<kDppXor2>(v);
-  v += dpp<kDppRor4>(v);
-  v += dpp<kDppRor8>(v);
-  return v;
-}
-
 template <int N>
 struct Log2 {
   static constexpr int v = (N >= 16) ? 4 : (N >= 8) ? 3 : (N >= 4) ? 2 : (N >= 2) ? 1 : 0;
