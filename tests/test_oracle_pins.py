@@ -558,6 +558,32 @@ def test_verify_rows_equal_sequential_decode(orc):
         np.testing.assert_array_equal(a.v, b.v)
 
 
+def test_speculative_rollback_leaves_no_trace(orc):
+    """Speculative decoding: a verify pass at p..p+R-1 whose drafts after the
+    first are rejected is followed by a pass at p+2.  Its rows write their own
+    K/V at p+2.. before attending, so the rejected drafts left at p+2, p+3 are
+    never read: the second pass is bit-identical to one over a cache that
+    never held them."""
+    R, past = 4, 6
+    dims, layers, kvs = attn_stack_with_cache(orc, R, R, past, seed=41)
+    _, _, fresh = attn_stack_with_cache(orc, R, R, past, seed=41)
+    rng = np.random.default_rng(42)
+    h1 = rng.standard_normal((R, 32)).astype(np.float32)
+    h2 = rng.standard_normal((R, 32)).astype(np.float32)
+    orc.forward(dims, layers, h1, positions=[past + r for r in range(R)], kvs=kvs, rows_per_seq=R)
+    p1 = past + 2  # token p and one draft accepted
+    after = [orc.OracleKV(kv.k.copy(), kv.v.copy()) for kv in kvs]
+    out_a, _ = orc.forward(dims, layers, h2, positions=[p1 + r for r in range(R)], kvs=after, rows_per_seq=R)
+    clean = [orc.OracleKV(kv.k.copy(), kv.v.copy()) for kv in kvs]
+    for c, f0 in zip(clean, fresh):
+        c.k[:, :, p1:past + R] = f0.k[:, :, p1:past + R]
+        c.v[:, :, p1:past + R] = f0.v[:, :, p1:past + R]
+    out_b, _ = orc.forward(dims, layers, h2, positions=[p1 + r for r in range(R)], kvs=clean, rows_per_seq=R)
+    np.testing.assert_array_equal(out_a, out_b)
+    # the rejected positions did hold the drafts (the check above is not vacuous)
+    assert not np.array_equal(kvs[0].k[:, :, p1:past + R], fresh[0].k[:, :, p1:past + R])
+
+
 def test_batched_sequences_equal_single(orc):
     """Rows of different sequences do not interact."""
     M, past = 3, 5
