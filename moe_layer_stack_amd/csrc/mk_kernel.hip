@@ -1107,13 +1107,13 @@ __device__ __forceinline__ float part_row(const float* part, int block, int q, i
 // run starting at tile i (and may reload the x registers); after a run with
 // round_end set, all waves synchronise and epi(first, last) runs over the
 // round's tiles.  The stream keeps issuing `nxt`'s tiles meanwhile.
-template <typename WT, int MT, int KC, int KN, class SegFn, class EpiFn>
+template <typename WT, int MT, int KC, int KN, bool kSettle = true, class SegFn, class EpiFn>
 __device__ __forceinline__ void run_gemv(Smem sm, Stream& st, const Plan& cur, const Plan& nxt, XRegs<WT, MT>& xr,
                                          SegFn seg, EpiFn epi) {
   constexpr int G = GroupOf<WT, MT>::G;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   st.mark(1);
-  settle();
+  if constexpr (kSettle) settle();
   st.fill<KC, KN>(sm, cur, nxt, 0, wave, lane);
   int round_first = 0;
   for (int i = 0; i < cur.n;) {
@@ -1700,7 +1700,7 @@ __device__ __forceinline__ void phase_rs(const KParams& p, Smem sm, int l, Strea
 // union of chosen experts.  Selection is on the logits, larger first, equal
 // logits ranked by lower expert id; weights are softmax probabilities
 // renormalised over the chosen set.
-__device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
+__device__ __forceinline__ void route_rank(const KParams& p, Smem sm, int l) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int E = p.E, k = p.k, M = p.M;
   const float* logits = act_f(p, l, p.al.logits);
@@ -1785,6 +1785,15 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
     if (lane == 0) ms->n_uni = __popcll(mm);
   }
   __syncthreads();
+}
+
+// The routing step's tables, after route_rank: uslot[u][t] (top-k slot of
+// union expert u in row t, or -1), umask[u] (its rows), and the trace.
+__device__ __forceinline__ void route_tables(const KParams& p, Smem sm, int l) {
+  const int E = p.E, k = p.k, M = p.M;
+  const float* logits = act_f(p, l, p.al.logits);
+  Misc* ms = sm.misc;
+  const int* rank_tab = reinterpret_cast<const int*>(res_slice(sm));
   const int n_uni = ms->n_uni;
   for (int it = threadIdx.x; it < kMaxExperts * kMaxRows; it += kThreads) {
     const int u = it / kMaxRows, t = it % kMaxRows;
@@ -1809,6 +1818,11 @@ __device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
     if (p.t_logits)
       for (int i = threadIdx.x; i < M * E; i += kThreads) p.t_logits[((size_t)l * p.Mt + p.row0) * E + i] = logits[i];
   }
+}
+
+__device__ __forceinline__ void route_topk(const KParams& p, Smem sm, int l) {
+  route_rank(p, sm, l);
+  route_tables(p, sm, l);
 }
 
 // x registers for one tile from LDS rows: token t uses row rows[t] of [M][..][F]
@@ -1865,24 +1879,30 @@ __device__ __forceinline__ void rg_stage(const KParams& p, Smem sm, int l) {
 // RG: shared-expert down projection y_s = sum_s Wd_s a_s (x from LDS), then
 // the routed gate/up rows for the union experts (x = y from RS):
 // a[t][slot][f] for the rows routed to the expert.
+// early: tiles of P issued after the shared activations' DMA (rg_stage),
+// before this call; 0 when none.  The wait below then leaves them in flight.
 template <typename WT, int MT>
 __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Stream& st, const Plan& P, const Plan& N,
-                                         const XRegs<WT, MT>& xr) {
+                                         const XRegs<WT, MT>& xr, int early) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int d = p.d, F = p.F, k = p.k, M = p.M, S = p.S;
   float* a = act_w(p, l, p.al.a);
   float* ys = act_w(p, l, p.al.y_s);
   // misc->rinv still holds RS's 1/rms of h1; the shared activations are on
-  // their way to LDS (rg_stage, issued before the routing step).
+  // their way to LDS (rg_stage, issued before the routing step).  This
+  // wave's part of them has landed once at most 2 * early of its vector
+  // memory operations are outstanding (they complete in order); no
+  // compiler-visible load is pending here, so the GEMV needs no full drain.
   zero_part(sm);
-  wait_all();
+  if (early > 0) wait_tiles_ahead(early);
+  else wait_all();
   __syncthreads();
   const Misc* ms = sm.misc;
   constexpr int kRound = (kPartAcc / (kWaves * Slots<WT>::C * MT)) & ~1;  // even: a gate/up pair stays in one round
   const int n1 = P.n1, n = P.n, nj = P.nj, lrb = P.lrb, lrb2 = P.lrb2, rpt = P.rpt, rpt2 = P.rpt2;
   const int fb_per = P.fb_per, sd_lo = P.lo, p_lo = P.lo2;
   XRegs<WT, MT> xw;  // a_s rows for the shared-down tiles, then y
-  run_gemv<WT, MT, PK_RG, MT == 1 ? PK_DOWN : PK_DOWNA>(
+  run_gemv<WT, MT, PK_RG, MT == 1 ? PK_DOWN : PK_DOWNA, false>(
       sm, st, P, N, xw,
       [&](int i, Seg<MT>& sg) {
         seg_all<MT>(sg, M);
@@ -2198,6 +2218,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   long long* stamp = p.stamps ? p.stamps + (size_t)blockIdx.x * 4 * (p.barriers + 1) : nullptr;
   XRegs<WT, MT> xr_moe;
   Stream st{0, 0, stamp, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring)};
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   // phase i owns slots 4i..4i+3: start (after barrier i), tile loop start,
   // tile loop end, end (before barrier i+1)
 #define MK_SYNC()                                   \
@@ -2242,10 +2263,14 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
     }
     {
       rg_stage(p, sm, l);
-      route_topk(p, sm, l);
+      route_rank(p, sm, l);
       cur = plan_rg<WT>(p, ms, l, true);  // same first tiles as the prefetched plan
       const Plan nxt = MT == 1 ? plan_down<WT>(p, ms, l) : plan_down_a<WT>(p, ms, l);
-      phase_rg<WT, MT>(p, sm, l, st, cur, nxt, xr_moe);
+      // the routed tiles start streaming as soon as the union is known
+      const int pre = st.issued;
+      st.fill<PK_RG, MT == 1 ? PK_DOWN : PK_DOWNA>(sm, cur, nxt, 0, wave, lane);
+      route_tables(p, sm, l);
+      phase_rg<WT, MT>(p, sm, l, st, cur, nxt, xr_moe, st.issued - pre);
       MK_SYNC();
       st.advance(cur);
       cur = nxt;
@@ -2312,7 +2337,7 @@ __global__ void __launch_bounds__(kThreads, 1) phase_step_kernel(KParams kp) {
                           p.d, p.eps, wave, lane, plan_rs<WT>(p, l).lrb);
       rg_stage(p, sm, l);
       route_topk(p, sm, l);
-      phase_rg<WT, MT>(p, sm, l, st, plan_rg<WT>(p, ms, l, true), none, xr);
+      phase_rg<WT, MT>(p, sm, l, st, plan_rg<WT>(p, ms, l, true), none, xr, 0);
       break;
     }
     case PH_DOWN:
