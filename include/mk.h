@@ -151,7 +151,11 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
  * stream) and return at once.  hidden_in [M][d] fp32, positions [M] int32,
  * hidden_out [M][d] fp32 are device pointers; hidden_out must not overlap
  * hidden_in.  kv may be NULL only for stacks without attention.  Errors:
- * INVALID_ARG, HIP. */
+ * INVALID_ARG, HIP.
+ * Each call stamps its launches with a new tag taken on the host, and the
+ * attention split combine accepts only words that carry it.  So a step
+ * captured into a HIP graph must not be replayed: every replay would carry
+ * the captured tag, and a replay could read the previous one's partials. */
 int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
                    float* hidden_out, void* stream);
 
