@@ -152,10 +152,9 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
  * hidden_out [M][d] fp32 are device pointers; hidden_out must not overlap
  * hidden_in.  kv may be NULL only for stacks without attention.  Errors:
  * INVALID_ARG, HIP.
- * Each call stamps its launches with a new tag taken on the host, and the
- * attention split combine accepts only words that carry it.  So a step
- * captured into a HIP graph must not be replayed: every replay would carry
- * the captured tag, and a replay could read the previous one's partials. */
+ * The call may be captured into a HIP graph and replayed: the launch tag that
+ * the attention split combine checks is taken on the device at launch start,
+ * so every replay gets a new one. */
 int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
                    float* hidden_out, void* stream);
 
@@ -175,7 +174,8 @@ int mk_decode_step_phased(mk_handle* h, const float* hidden_in, const int32_t* p
 int mk_destroy(mk_handle* h);
 
 /* Wait for `stream` and report (then clear) any device-side error of this
- * handle's steps: TIMEOUT or INVALID_ARG. */
+ * handle's steps: TIMEOUT or INVALID_ARG.  Clearing resets the barrier state
+ * and zeroes the handle's workspace. */
 int mk_sync(mk_handle* h, void* stream);
 
 /* Record routing per step into device buffers (any may be NULL; all NULL

@@ -75,6 +75,7 @@ struct SyncLayout {
   static constexpr int kGlobal = 0;
   static constexpr int kEpoch = 1 * kLine;
   static constexpr int kErr = 2 * kLine;
+  static constexpr int kTag = 3 * kLine;     // tag epoch: launch-tagged words carry this + 1
   static constexpr int kGroup = 4 * kLine;   // 8 group counters
   static constexpr int kFlag = 12 * kLine;   // 8 group release flags
   static constexpr int kWords = 20 * kLine;
@@ -108,7 +109,6 @@ struct KParams {
   char* act;
   ActLayout al;
   unsigned* sync;            // SyncLayout
-  unsigned tag;              // this launch's tag (nonzero; differs from every earlier launch on the handle)
   long long* stamps;         // [n_cu][4*(barriers+1)] or null
   int* t_ids;
   float* t_w;

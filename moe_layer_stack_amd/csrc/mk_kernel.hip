@@ -189,6 +189,7 @@ struct Misc {
   int flag;
   int last;
   int epoch;
+  unsigned tag;         // this launch's tag: the tag epoch at launch start, plus one
   int gbad[2][kWaves];  // split combine: per wave, words not yet of this launch (by round parity)
   float rinv[kMaxRows];
   float ssq[kWaves * kMaxRows];
@@ -1242,7 +1243,7 @@ __device__ __forceinline__ void attn_gather(const KParams& p, Smem sm, int l, in
       for (int u = 0; u < 4; ++u) {
         const int it = b0 + u * kThreads;
         if (it < nload) {
-          if ((unsigned)(v[u] >> 32) != p.tag) bad = 1;
+          if ((unsigned)(v[u] >> 32) != ms->tag) bad = 1;
           else scr[it] = __uint_as_float((unsigned)v[u]);
         }
       }
@@ -1595,8 +1596,8 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
       float L = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) L += cw[w] * wst[(size_t)(w * NQ + q) * kPartStride + 1];
-      st_tag(dst + 0, M, p.tag);
-      st_tag(dst + 1, L, p.tag);
+      st_tag(dst + 0, M, ms->tag);
+      st_tag(dst + 1, L, ms->tag);
     } else {
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1604,8 +1605,8 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
         const float* src = wst + (size_t)(w * NQ + q) * kPartStride + 4 + 4 * k4;
         a.x += cw[w] * src[0]; a.y += cw[w] * src[1]; a.z += cw[w] * src[2]; a.w += cw[w] * src[3];
       }
-      st_tag(dst + 4 + 4 * k4, a.x, p.tag); st_tag(dst + 5 + 4 * k4, a.y, p.tag);
-      st_tag(dst + 6 + 4 * k4, a.z, p.tag); st_tag(dst + 7 + 4 * k4, a.w, p.tag);
+      st_tag(dst + 4 + 4 * k4, a.x, ms->tag); st_tag(dst + 5 + 4 * k4, a.y, ms->tag);
+      st_tag(dst + 6 + 4 * k4, a.z, ms->tag); st_tag(dst + 7 + 4 * k4, a.w, ms->tag);
     }
   }
   __syncthreads();  // the wave states are read before the gather reuses the x region
@@ -2184,6 +2185,12 @@ __device__ __forceinline__ bool launch_setup(const KParams& p, Smem sm) {
           if (ms->pos[r] == ms->pos[r2]) bad |= kErrDupPosition;
     ms->flag = bad;
     ms->epoch = (int)ld_dev(p.sync + SyncLayout::kEpoch);
+    // The tag epoch changes only where no block of a launch that uses tags
+    // can still read it (after the persistent kernel's last grid barrier; in
+    // phase launches other than attention), so all blocks of a launch read
+    // the same value.  Taken on the device, it also differs between replays
+    // of a captured graph.
+    ms->tag = ld_dev(p.sync + SyncLayout::kTag) + 1u;
   }
   __syncthreads();
   if (ms->flag) {
@@ -2296,7 +2303,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
 #undef MK_SYNC
   wait_all();
   st.mark(3);
-  if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u(p.sync + SyncLayout::kEpoch, epoch0 + b);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    st_dev_u(p.sync + SyncLayout::kEpoch, epoch0 + b);
+    st_dev_u(p.sync + SyncLayout::kTag, ms->tag);  // every block read the tag epoch before the first barrier
+  }
 }
 
 // One phase of one layer per launch: the same phase code as the persistent
@@ -2358,6 +2368,9 @@ __global__ void __launch_bounds__(kThreads, 1) phase_step_kernel(KParams kp) {
       break;
   }
   wait_all();
+  // a launch without tagged words moves the tag epoch on: a late block of
+  // this launch may read either value, which no phase here depends on
+  if (p.only_ph != PH_ATTN && blockIdx.x == 0 && threadIdx.x == 0) st_dev_u(p.sync + SyncLayout::kTag, ms->tag);
 }
 
 }  // namespace mk

@@ -60,7 +60,6 @@ struct mk_handle {
   char* d_act = nullptr;
   unsigned* d_sync = nullptr;
   size_t act_bytes = 0;
-  unsigned launch_tag = 0;  // tag of the last launch; the workspace starts zeroed, so 0 is never used
   int32_t* t_ids = nullptr;
   float* t_w = nullptr;
   float* t_logits = nullptr;
@@ -381,8 +380,6 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
     p.act = h->d_act;
     p.al = h->al;
     p.sync = h->d_sync;
-    if (++h->launch_tag == 0) h->launch_tag = 1;
-    p.tag = h->launch_tag;
     p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
     if (!phased) {
       p.stamps = reinterpret_cast<long long*>(h->stamps);
@@ -429,8 +426,11 @@ int mk_sync(mk_handle* h, void* stream) {
   e = hipMemcpy(&err, h->d_sync + SyncLayout::kErr, 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(MK_ERR_HIP, "reading the device error flag failed: %s", hipGetErrorString(e));
   if (err == 0) return MK_OK;
-  // reset barrier state and counters so the handle can run again
-  if (hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+  // reset barrier state, counters and the tag epoch so the handle can run
+  // again; the workspace is cleared with it, so that no word tagged before
+  // the reset can carry a tag that the restarted epoch hands out again
+  if (hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess ||
+      hipMemset(h->d_act, 0, h->act_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
     return fail(MK_ERR_HIP, "resetting the barrier state failed");
   if (err & mk::kErrTimeout) return fail(MK_ERR_TIMEOUT, "a grid barrier timed out (device flag 0x%x)", err);
   return fail(MK_ERR_INVALID_ARG, "a position was outside the cache or repeated within a sequence (flag 0x%x)", err);
