@@ -21,8 +21,8 @@ Other legs, reported beside the headline: batch 8 over the same weights; the
 verify pass (1 and 8 sequences x 8 rows); speculative decoding around the
 verify pass with a synthetic acceptance process (effective tokens/s at about
 6 tokens per step); the same step as one kernel launch per phase of every
-layer (the many-kernels baseline, batch 1 and 8); the 16-layer MoE-only
-stack at batch 1 and 8.
+layer (the many-kernels baseline, batch 1 and 8, and at batch 1 replayed
+from a HIP graph); the 16-layer MoE-only stack at batch 1 and 8.
 
 HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
 this script with --calib-copy-mib, one with --pmc FETCH_SIZE and one with
@@ -186,6 +186,43 @@ def spec_leg(torch, mk, st, w, n_seq, steps, warmup, alpha=0.9155, seed=5):
     return dict(sequences=n_seq, rows=M, ms_per_step=ms, tokens_per_step=float(np.mean(toks)) / n_seq,
                 effective_tok_s=float(np.sum(toks)) / (ms * 1e-3 * len(ev)), accept_alpha=alpha,
                 finite=bool(torch.isfinite(out).all().item()))
+
+
+def graph_leg(torch, mk, st, w, M, steps, warmup):
+    """The one-launch-per-phase step captured once into a HIP graph and
+    replayed: the launches keep their boundaries (no prefetch across them)
+    but lose the host's launch gaps.  Each replay is timed by events on the
+    replay stream."""
+    import numpy as np
+    h = mk.mk_create(st.config(rows=M, rows_per_seq=1), st.layer_weights())
+    s = torch.cuda.Stream()
+    hin = st.hidden(0, rows=M)
+    hout = torch.empty_like(hin)
+    pos = torch.tensor([w.past] * M, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        mk.mk_decode_step_phased(h, hin.data_ptr(), pos.data_ptr(), st.kv(), hout.data_ptr(), s.cuda_stream)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mk.mk_decode_step_phased(h, hin.data_ptr(), pos.data_ptr(), st.kv(), hout.data_ptr(), s.cuda_stream)
+    torch.cuda.synchronize()
+    ev = []
+    for t in range(warmup + steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            a.record(s)
+            g.replay()
+            b.record(s)
+        if t >= warmup:
+            ev.append((a, b))
+    torch.cuda.synchronize()
+    rc = mk.mk_sync(h, 0)
+    del g
+    mk.mk_destroy(h)
+    if rc != mk.MK_OK:
+        raise mk.MkError(rc, mk.mk_last_error())
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
 def moe16_legs(torch, mk, steps, warmup):
@@ -386,6 +423,11 @@ def main():
                 f"({100 * r['frac']:.1f}% of peak); the persistent kernel: "
                 f"{ref['ms_per_step'] if ref else float('nan'):.3f} ms/step")
             phased[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        g_ms = graph_leg(torch, mk, st, w1, 1, min(args.steps, 10), 2)
+        log(f"phased_b1 replayed from a HIP graph: {g_ms:.3f} ms/step ({g_ms / b1['ms_per_step']:.2f} x the "
+            f"persistent kernel)")
+        phased["phased_graph_b1"] = {"ms_per_step": round(g_ms, 4), "tok_s": round(1e3 / g_ms, 3),
+                                     "launches": phased["phased_b1"]["launches"] if "phased_b1" in phased else None}
     moe16 = {}
     if not args.no_moe16:
         moe16 = moe16_legs(torch, mk, args.moe16_steps, args.warmup)
