@@ -2375,31 +2375,43 @@ __global__ void __launch_bounds__(kThreads, 1) phase_step_kernel(KParams kp) {
 
 }  // namespace mk
 
-// kernel of (weight dtype, token group, attention task kind) for a launch
+// kernel of (weight dtype, token group, attention task kind) for a launch.
+// The token group follows the row count: one row takes the single-row
+// kernel, whose DOWN is one phase; more rows take the 8-row kernel, whose
+// DOWN runs as two phases over the per-expert partials.  The host sizes the
+// barriers, the partial buffer and the per-phase launches by that same rule,
+// so an 8-row kernel never runs a single row.
+constexpr int kKernelKinds = 6;
 static int mk_pick(const mk::KParams& p, bool phased, const void** fn, int* idx) {
   using namespace mk;
-  if (p.M > kMaxRows) return -2;
+  if (p.M < 1 || p.M > kMaxRows) return -2;
   if (p.attn && p.n_seq * p.G * p.q_groups * p.n_splits > p.n_cu) return -2;
   const int Q = p.attn ? p.q_per_task : 0;
+  const bool one = p.M == 1;
   // instantiations: weight dtype x token group (1 or 8) x attention task
-  // kind (1: at most 4 query vectors, decode; 2: at most 16, verify)
+  // kind (1: at most 4 query vectors; 2: at most 16, several rows of a
+  // sequence or many query heads per kv head)
+  static const void* const persistent[kKernelKinds] = {
+      (const void*)decode_step_kernel<float, 1, 1>,    (const void*)decode_step_kernel<float, 8, 1>,
+      (const void*)decode_step_kernel<uint16_t, 1, 1>, (const void*)decode_step_kernel<uint16_t, 8, 1>,
+      (const void*)decode_step_kernel<uint16_t, 1, 2>, (const void*)decode_step_kernel<uint16_t, 8, 2>};
+  static const void* const per_phase[kKernelKinds] = {
+      (const void*)phase_step_kernel<float, 1, 1>,    (const void*)phase_step_kernel<float, 8, 1>,
+      (const void*)phase_step_kernel<uint16_t, 1, 1>, (const void*)phase_step_kernel<uint16_t, 8, 1>,
+      (const void*)phase_step_kernel<uint16_t, 1, 2>, (const void*)phase_step_kernel<uint16_t, 8, 2>};
+  int k;
   if (p.wide) {
     if (Q > 4) return -2;
-    if (phased) *fn = p.M == 1 ? (const void*)phase_step_kernel<float, 1, 1> : (const void*)phase_step_kernel<float, 8, 1>;
-    else *fn = p.M == 1 ? (const void*)decode_step_kernel<float, 1, 1> : (const void*)decode_step_kernel<float, 8, 1>;
-    *idx = p.M == 1 ? 0 : 1;
+    k = 0;
   } else if (Q <= 4) {
-    if (phased)
-      *fn = p.M == 1 ? (const void*)phase_step_kernel<uint16_t, 1, 1> : (const void*)phase_step_kernel<uint16_t, 8, 1>;
-    else
-      *fn = p.M == 1 ? (const void*)decode_step_kernel<uint16_t, 1, 1> : (const void*)decode_step_kernel<uint16_t, 8, 1>;
-    *idx = p.M == 1 ? 2 : 3;
+    k = 2;
   } else {
-    if (Q > 16) return -2;
-    *fn = phased ? (const void*)phase_step_kernel<uint16_t, 8, 2> : (const void*)decode_step_kernel<uint16_t, 8, 2>;
-    *idx = 4;
+    if (Q > kMaxQTask) return -2;
+    k = 4;
   }
-  if (phased) *idx += 5;
+  k += one ? 0 : 1;
+  *fn = phased ? per_phase[k] : persistent[k];
+  *idx = k + (phased ? kKernelKinds : 0);
   return 0;
 }
 
@@ -2411,7 +2423,7 @@ extern "C" int mk_launch_kernel(const mk::KParams* pp, void* stream) {
   int idx = 0;
   const int pk = mk_pick(p, p.only_ph >= 0, &fn, &idx);
   if (pk != 0) return pk;
-  static bool attr_done[10] = {false, false, false, false, false, false, false, false, false, false};
+  static bool attr_done[2 * kKernelKinds] = {};
   if (!attr_done[idx]) {
     // the kernel takes all of the CU's LDS dynamically: any static LDS (a
     // library routine that declares its own) would make the launch fail
