@@ -187,6 +187,11 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
                   "groups of at most %d", Qall, mk::kMaxQTask);
     }
     h->q_task = Qall / h->q_groups;
+    if (n_seq * G * h->q_groups > h->n_cu) {  // one attention task per CU at least
+      delete h;
+      return fail(MK_ERR_UNSUPPORTED, "%d sequences x %d kv heads x %d query groups exceed the %d CUs", n_seq, G,
+                  h->q_groups, h->n_cu);
+    }
     int s = h->n_cu / (n_seq * G * h->q_groups);
     if (s < 1) s = 1;
     int maxs = (c.kv_capacity + mk::kAttnTile - 1) / mk::kAttnTile;

@@ -94,6 +94,30 @@ def test_create_rejects_bad_config(mk, kw, status):
     assert ei.value.status == status, str(ei.value)
 
 
+def test_create_rejects_too_many_queries_per_kv_head(mk):
+    # 8 verify rows of one sequence with 8 query heads per kv head: 64 query
+    # vectors per (sequence, kv head), above the 32 an attention task set holds
+    kw = dict(dtype=1, d_model=1024, d_ff=1024, has_attn=1, n_heads=32, n_kv_heads=4, head_dim=128,
+              rows=8, rows_per_seq=8, kv_capacity=64)
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_create(_cfg(mk, **kw), _layers(2))
+    assert ei.value.status == -2 and "rows_per_seq * n_heads / n_kv_heads" in mk.mk_last_error()
+    # the same with 4 rows per sequence (32 queries) passes validation and
+    # stops at the next check, the (absent) attention weights of the stand-in layers
+    kw.update(rows_per_seq=4)
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_create(_cfg(mk, **kw), _layers(2))
+    assert ei.value.status == mk.MK_ERR_INVALID_ARG and "attention weight pointer" in mk.mk_last_error()
+
+
+def test_create_rejects_fp32_wide_query_groups(mk):
+    kw = dict(dtype=0, d_model=1024, d_ff=512, has_attn=1, n_heads=16, n_kv_heads=2, head_dim=128,
+              kv_capacity=64)
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_create(_cfg(mk, **kw), _layers(2))
+    assert ei.value.status == -2 and "fp32" in mk.mk_last_error()
+
+
 def test_create_rejects_null_weights(mk):
     from moe_layer_stack_amd import mk_layer_weights
     lw = [mk_layer_weights() for _ in range(2)]

@@ -59,14 +59,25 @@ def test_shared_expert_counts(env, n_shared, M):
     _parity(env, w)
 
 
-@pytest.mark.parametrize("G,M,L", [(4, 1, 3), (4, 8, 2), (2, 1, 3)])
+@pytest.mark.parametrize("G,M,L", [(4, 1, 3), (4, 8, 2), (2, 1, 3), (1, 1, 2)])
 def test_fewer_kv_heads(env, G, M, L):
+    # G = 1 (one kv head for all 32 query heads): 32 queries per task at one
+    # row, in two groups of 16
     from synth.workloads import ATTN92_B1
     w = ATTN92_B1.with_(name=f"attn_g{G}_m{M}", L=L, G=G, M=M, input_seed=8)
     _parity(env, w)
 
 
-@pytest.mark.parametrize("G", [4, 2])
+@pytest.mark.parametrize("G,rps", [(4, 4), (2, 2)])
+def test_verify_fewer_kv_heads(env, G, rps):
+    # 8 rows as 8 / rps sequences of rps verify rows: rps * 32 / G = 32 queries
+    # per (sequence, kv head), in two groups of 16
+    from synth.workloads import VERIFY92_M8
+    w = VERIFY92_M8.with_(name=f"verify_g{G}_rps{rps}", L=2, G=G, rows_per_seq=rps, input_seed=8)
+    _parity(env, w)
+
+
+@pytest.mark.parametrize("G", [4, 2, 1])
 def test_fewer_kv_heads_phased_equals_persistent(env, G):
     import moe_layer_stack_amd as mk
     from synth.stack import DeviceStack
