@@ -77,6 +77,16 @@ def test_verify_fewer_kv_heads(env, G, rps):
     _parity(env, w)
 
 
+@pytest.mark.parametrize("M,rps", [(3, 1), (6, 3), (5, 1)])
+def test_odd_row_counts(env, M, rps):
+    # row counts between 1 and 8 run the 8-row kernel on M rows; 3 verify rows
+    # of 4 heads give 12 queries per (sequence, kv head), a partly filled
+    # 16-query operand
+    from synth.workloads import ATTN92_B1
+    w = ATTN92_B1.with_(name=f"attn_m{M}_rps{rps}", L=2, M=M, rows_per_seq=rps, input_seed=10)
+    _parity(env, w)
+
+
 @pytest.mark.parametrize("G", [4, 2, 1])
 def test_fewer_kv_heads_phased_equals_persistent(env, G):
     import moe_layer_stack_amd as mk
