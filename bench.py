@@ -256,14 +256,17 @@ def moe16_legs(torch, mk, steps, warmup):
     return out
 
 
-def cpu_baseline(torch, st, w, n_layers_sample):
+def cpu_baseline(torch, st, w, n_layers_sample, threads=None):
     """The CPU oracle (as it stands) on the first layers of a batch-1 step:
-    host copies of the touched tensors are made before the timer starts."""
+    host copies of the touched tensors are made before the timer starts.
+    threads: the oracle's thread count for this sample (default: all)."""
     import numpy as np
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from parity_util import dims_of, oracle_layer
     dims = dims_of(w)
+    all_threads = oracle.num_threads()
+    used = oracle.set_threads(threads) if threads else all_threads
     h = st.hidden(0)[:1].cpu().numpy().astype(np.float64)
     pos = [w.past]
     t_compute = 0.0
@@ -280,9 +283,11 @@ def cpu_baseline(torch, st, w, n_layers_sample):
         t0 = time.perf_counter()
         h = oracle.moe_block(dims, ly, h1, ids, wts)
         t_compute += time.perf_counter() - t0
+    if threads:
+        oracle.set_threads(all_threads)
     per_layer = t_compute / n_layers_sample
     step_s = per_layer * w.L
-    return dict(value=1.0 / step_s, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    return dict(value=1.0 / step_s, unit="tokens/s", cores=used, kind="oracle",
                 sample=f"first {n_layers_sample} of {w.L} layers of one batch-1 step (fp64 C oracle, OpenMP over "
                        f"output rows); compute time {t_compute:.1f} s, scaled by {w.L}/{n_layers_sample}")
 
@@ -345,6 +350,8 @@ def main():
     ap.add_argument("--no-phased", action="store_true", help="skip the one-launch-per-phase baseline legs")
     ap.add_argument("--moe16-steps", type=int, default=256, help="timed steps of the 16-layer legs")
     ap.add_argument("--cpu-layers", type=int, default=92, help="layers in the CPU-oracle sample (default: a whole step)")
+    ap.add_argument("--cpu-layers-1t", type=int, default=12,
+                    help="layers in the single-thread CPU-oracle sample (0: skip it)")
     ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the workload's 92)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed legs, one device copy of this size (counter calibration)")
@@ -463,6 +470,11 @@ def main():
             t0 = time.perf_counter()
             cpu = cpu_baseline(torch, st, w1, min(args.cpu_layers, st.L))
             log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads ({time.perf_counter() - t0:.1f} s)")
+            if args.cpu_layers_1t > 0:
+                t0 = time.perf_counter()
+                one = cpu_baseline(torch, st, w1, min(args.cpu_layers_1t, st.L), threads=1)
+                cpu["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+                log(f"cpu oracle, one thread: {one['value']:.4f} tok/s ({time.perf_counter() - t0:.1f} s)")
         optional("cpu_baseline", cpu_leg)
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4

@@ -69,7 +69,9 @@ def lib():
         L.orc_forward.argtypes = [C.POINTER(Dims), C.c_int, C.POINTER(Layer), C.c_int, C.c_int,
                                   C.POINTER(C.c_int32), C.POINTER(KV), C.POINTER(C.c_float),
                                   C.POINTER(C.c_float), dp, ip, dp, dp]
-        for f in ("orc_attn_block", "orc_route", "orc_moe_block", "orc_forward", "orc_num_threads"):
+        L.orc_set_threads.argtypes = [C.c_int]
+        for f in ("orc_attn_block", "orc_route", "orc_moe_block", "orc_forward", "orc_num_threads",
+                  "orc_set_threads"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -103,6 +105,12 @@ def _vp(a):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's parallel loops from now on (results do not
+    depend on it); returns the count in effect."""
+    return lib().orc_set_threads(int(n))
 
 
 def bf16_to_double(bits: int) -> float:

@@ -41,6 +41,18 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads of the next parallel loops (timing only: every output is summed
+   in the same fixed order whatever the thread count). */
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 /* bf16 is the upper half of an IEEE binary32: widening is exact. */
 double orc_bf16_to_double(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;

@@ -137,6 +137,7 @@ int orc_forward(const orc_dims* dm, int L, const orc_layer* layers, int M, int r
 
 /* threads the oracle's parallel loops use (1 when built without OpenMP) */
 int orc_num_threads(void);
+int orc_set_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -162,6 +162,49 @@ def test_bad_positions_are_reported_and_the_handle_recovers(env):
         run.close()
 
 
+def test_host_side_argument_errors_launch_nothing(env):
+    """Arguments the host can check are refused before any launch, for both
+    entry points: hidden_out overlapping hidden_in (the same buffer, or one
+    row apart), a NULL positions pointer, a KV cache of another capacity.
+    The output stays untouched and the handle's next step is unchanged."""
+    import moe_layer_stack_amd as mk
+    from moe_layer_stack_amd import mk_kv_cache
+    from parity_util import GpuRun
+    from synth.workloads import ATTN92_B8
+    torch = env
+    w = ATTN92_B8
+    _say(f"host-side argument errors {w.name} L=2")
+    st = _stack(w, 2)
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        good = run.step(hid, w.positions(0)).clone()
+        pos = torch.as_tensor(np.asarray(w.positions(0), dtype=np.int32), device="cuda")
+        big = torch.zeros(w.M + 1, w.d, dtype=torch.float32, device="cuda")
+        big[:w.M].copy_(hid)
+        wrong_cap = mk_kv_cache(st.kc.data_ptr(), st.vc.data_ptr(), w.n_seq, w.capacity + 1)
+        out = torch.full_like(hid, 7.0)
+        cases = [
+            ("same buffer", hid.data_ptr(), pos.data_ptr(), st.kv(), hid.data_ptr(), "overlaps"),
+            ("one row apart", big.data_ptr(), pos.data_ptr(), st.kv(), big[1:].data_ptr(), "overlaps"),
+            ("NULL positions", hid.data_ptr(), 0, st.kv(), out.data_ptr(), "NULL"),
+            ("capacity", hid.data_ptr(), pos.data_ptr(), wrong_cap, out.data_ptr(), "capacity"),
+        ]
+        for fn in (mk.mk_decode_step, mk.mk_decode_step_phased):
+            for name, a, p_, kv, b, msg in cases:
+                with pytest.raises(mk.MkError) as ei:
+                    fn(run.h, a, p_, kv, b, 0)
+                assert ei.value.status == mk.MK_ERR_INVALID_ARG and msg in mk.mk_last_error(), (name, str(ei.value))
+        torch.cuda.synchronize()
+        assert mk.mk_sync(run.h, 0) == mk.MK_OK
+        assert (out == 7.0).all()
+        assert torch.equal(big[:w.M], hid)
+        again = run.step(hid, w.positions(0))
+        assert torch.equal(again, good)
+    finally:
+        run.close()
+
+
 def test_batch8_row_equals_batch1(env):
     """Sequences are independent: row 0 of a batch-8 step equals the batch-1
     step of sequence 0 (same row, same position, same cache)."""
