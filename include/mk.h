@@ -87,14 +87,21 @@ typedef struct mk_config {
   int32_t d_model;         /* d: row length 1, 2, 4 or 8 KiB in the weight dtype */
   int32_t n_experts;       /* E, 1..64 */
   int32_t top_k;           /* k, 1..min(E, 8) */
-  int32_t n_shared;        /* always-on shared experts, weight 1; 0..4 */
+  int32_t n_shared;        /* always-on shared experts, weight 1; 0..4, and
+                              min(rows, 8) * n_shared * d_ff * 4 <= 39424 bytes */
   int32_t d_ff;            /* F: row length of w_down, 1, 2, 4 or 8 KiB */
   int32_t dtype;           /* mk_dtype of matrices and norm gains */
   int32_t has_router_bias; /* b_router must be non-NULL when set */
   float rms_eps;           /* > 0 */
   int32_t has_attn;        /* 0: MoE-only layers (h1 = h) */
-  int32_t n_heads;         /* H (attention stacks) */
-  int32_t n_kv_heads;      /* G, H % G == 0, H / G <= 8 */
+  int32_t n_heads;         /* H (attention stacks); H * head_dim rows of 2, 4 or 8
+                              KiB in bf16 (1..8 KiB in fp32) */
+  int32_t n_kv_heads;      /* G, H % G == 0.  Q = rows_per_seq * H / G query vectors
+                              per (sequence, kv head): Q <= 32, and Q <= 4 for fp32
+                              stacks.  Each (sequence, kv head) takes 1 attention
+                              task when Q <= 4, else n = ceil(Q / 16) tasks of Q / n
+                              queries (n must divide Q); sequences * G * n per
+                              launch must not outnumber the CUs */
   int32_t head_dim;        /* hd = 128 */
   float rope_theta;        /* > 0 */
   int32_t rows;            /* M, 1..64, fixed per handle.  Above 8, a multiple of 8 with
