@@ -117,4 +117,8 @@ struct KParams {
 
 }  // namespace mk
 
+// One cooperative launch of the kernel that p selects.  Returns 0, a
+// hipError_t of the launch (> 0), -1 (device query or the dynamic-LDS
+// attribute failed), -2 (geometry outside the instantiations) or -3 (the
+// kernel declares static LDS).
 extern "C" int mk_launch_kernel(const mk::KParams* p, void* stream);

@@ -2423,14 +2423,21 @@ extern "C" int mk_launch_kernel(const mk::KParams* pp, void* stream) {
   int idx = 0;
   const int pk = mk_pick(p, p.only_ph >= 0, &fn, &idx);
   if (pk != 0) return pk;
-  static bool attr_done[2 * kKernelKinds] = {};
-  if (!attr_done[idx]) {
+  // The dynamic-LDS limit is a per-device attribute of each kernel: set it
+  // once per (device, kernel); devices beyond the table set it every launch.
+  // Concurrent first launches may both set it, which is harmless.
+  constexpr int kAttrDevices = 16;
+  static bool attr_done[kAttrDevices][2 * kKernelKinds] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  bool* done = (dev >= 0 && dev < kAttrDevices) ? &attr_done[dev][idx] : nullptr;
+  if (!done || !*done) {
     // the kernel takes all of the CU's LDS dynamically: any static LDS (a
     // library routine that declares its own) would make the launch fail
     hipFuncAttributes fa;
     if (hipFuncGetAttributes(&fa, fn) != hipSuccess || fa.sharedSizeBytes != 0) return -3;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return -1;
-    attr_done[idx] = true;
+    if (done) *done = true;
   }
   void* args[] = {&p};
   hipError_t e = hipLaunchCooperativeKernel(fn, dim3(p.n_cu), dim3(kThreads), args, (unsigned)lds, (hipStream_t)stream);

@@ -329,6 +329,7 @@ namespace {
 int launch_status(int e) {
   if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
   if (e == -3) return fail(MK_ERR_HIP, "the kernel declares static LDS, which leaves no room for its ring");
+  if (e == -1) return fail(MK_ERR_HIP, "querying the device or setting the kernel's dynamic LDS limit failed");
   if (e != 0) return fail(MK_ERR_HIP, "launch failed: %s", hipGetErrorString((hipError_t)e));
   return MK_OK;
 }
