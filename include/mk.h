@@ -196,8 +196,10 @@ int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits);
  * i, into slots 4i .. 4i+3: the phase start (after the preceding grid
  * barrier), the start and the end of its weight-tile loop, and the phase end
  * (before the next barrier).  Phases in order per layer: QKV, ATTN, WO
- * (attention stacks), RS, RG, DOWN.  A step of more than 8 rows leaves the
- * stamps of its last launch. */
+ * (attention stacks), RS, RG, DOWN; with more than one row DOWN is two
+ * phases (the expert-major products, then the column sums, which stream no
+ * tiles and may leave their loop slots unset).  A step of more than 8 rows
+ * leaves the stamps of its last launch. */
 int mk_set_timing(mk_handle* h, int64_t* stamps);
 
 /* Launch geometry and workspace size of a handle. */

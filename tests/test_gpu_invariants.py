@@ -205,6 +205,52 @@ def test_host_side_argument_errors_launch_nothing(env):
         run.close()
 
 
+@pytest.mark.parametrize("name,G,M", [("attn92_b1", 8, 1), ("attn92_b8", 8, 8), ("attn92_b1", 4, 1)])
+def test_timing_stamps_fill_their_buffer_exactly(env, name, G, M):
+    """mk_set_timing: the kernel writes [n_cu][4 * (barriers + 1)] stamps and
+    nothing past them (a guard region stays at its sentinel); each phase's
+    start and end stamps are set and in time order per workgroup, the tile
+    loop's stamps (where written) inside them; the output equals the untimed
+    step bit for bit."""
+    import moe_layer_stack_amd as mk
+    from parity_util import GpuRun
+    from synth.workloads import ALL
+    torch = env
+    w = ALL[name].with_(G=G, M=M)
+    _say(f"timing stamps {w.name} G={G} M={M} L=2")
+    st = _stack(w, 2)
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        plain = run.step(hid, w.positions(0)).clone()
+        info = mk.mk_get_info(run.h)
+        n_cu, nb = info.n_cu, info.barriers_per_step
+        per = 4 * (nb + 1)
+        guard = 4096
+        sentinel = -7
+        buf = torch.full((n_cu * per + guard,), sentinel, dtype=torch.int64, device="cuda")
+        buf[:n_cu * per].zero_()
+        mk.mk_set_timing(run.h, buf.data_ptr())
+        timed = run.step(hid, w.positions(0))
+        mk.mk_set_timing(run.h, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(timed, plain)
+        b = buf.cpu().numpy()
+        assert (b[n_cu * per:] == sentinel).all(), "stamps written past the buffer"
+        t = b[:n_cu * per].reshape(n_cu, nb + 1, 4)
+        start, end = t[:, :, 0], t[:, :, 3]
+        assert (start > 0).all() and (end > 0).all(), "a phase start or end stamp is missing"
+        assert (end >= start).all()
+        assert (start[:, 1:] >= end[:, :-1]).all(), "phases out of order within a workgroup"
+        for k in (1, 2):
+            v = t[:, :, k]
+            ok = (v == 0) | ((v >= start) & (v <= end))
+            assert ok.all(), f"tile-loop stamp {k} outside its phase"
+        _say(f"timing stamps {w.name} G={G} M={M}: {n_cu} x {nb + 1} phases, guard intact")
+    finally:
+        run.close()
+
+
 def test_batch8_row_equals_batch1(env):
     """Sequences are independent: row 0 of a batch-8 step equals the batch-1
     step of sequence 0 (same row, same position, same cache)."""
