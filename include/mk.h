@@ -202,6 +202,15 @@ int mk_set_trace(mk_handle* h, int32_t* ids, float* w, float* logits);
  * leaves the stamps of its last launch. */
 int mk_set_timing(mk_handle* h, int64_t* stamps);
 
+/* Device watchdog of the handle's later steps, in ticks of the 100 MHz
+ * device realtime counter (default 200,000,000: 2 s); ticks >= 1, else
+ * INVALID_ARG.  Every grid-barrier poll and split-combine wait of a step gives
+ * up after this long: the step then ends early on every workgroup, its output
+ * and cache rows are undefined, and the next mk_sync returns TIMEOUT and
+ * resets the handle, which stays usable.  A limit far below a step's barrier
+ * latency (a few ticks) forces that path, for tests of error handling. */
+int mk_set_watchdog(mk_handle* h, int64_t ticks);
+
 /* Launch geometry and workspace size of a handle. */
 int mk_get_info(const mk_handle* h, mk_info* info);
 

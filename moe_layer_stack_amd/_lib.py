@@ -18,7 +18,7 @@ MK_ERR_TIMEOUT = -5
 MK_F32, MK_BF16 = 0, 1
 
 EXPORTS = ("mk_create", "mk_decode_step", "mk_decode_step_phased", "mk_destroy", "mk_sync", "mk_set_trace", "mk_set_timing",
-           "mk_get_info", "mk_strerror", "mk_last_error")
+           "mk_set_watchdog", "mk_get_info", "mk_strerror", "mk_last_error")
 
 
 class MkError(RuntimeError):
@@ -68,13 +68,14 @@ def lib():
         L.mk_sync.argtypes = [C.c_void_p, C.c_void_p]
         L.mk_set_trace.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         L.mk_set_timing.argtypes = [C.c_void_p, C.c_void_p]
+        L.mk_set_watchdog.argtypes = [C.c_void_p, C.c_int64]
         L.mk_get_info.argtypes = [C.c_void_p, C.POINTER(mk_info)]
         L.mk_strerror.argtypes = [C.c_int]
         L.mk_strerror.restype = C.c_char_p
         L.mk_last_error.argtypes = []
         L.mk_last_error.restype = C.c_char_p
         for f in ("mk_create", "mk_decode_step", "mk_decode_step_phased", "mk_destroy", "mk_sync", "mk_set_trace",
-                  "mk_set_timing", "mk_get_info"):
+                  "mk_set_timing", "mk_set_watchdog", "mk_get_info"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -130,6 +131,10 @@ def mk_set_trace(h, ids: int = 0, w: int = 0, logits: int = 0) -> int:
 
 def mk_set_timing(h, stamps: int = 0) -> int:
     return _check(lib().mk_set_timing(h, C.c_void_p(stamps or None)))
+
+
+def mk_set_watchdog(h, ticks: int) -> int:
+    return _check(lib().mk_set_watchdog(h, C.c_int64(int(ticks))))
 
 
 def mk_get_info(h) -> mk_info:

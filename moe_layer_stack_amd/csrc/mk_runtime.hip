@@ -64,6 +64,7 @@ struct mk_handle {
   float* t_w = nullptr;
   float* t_logits = nullptr;
   int64_t* stamps = nullptr;
+  long long watchdog_ticks = 200LL * 1000 * 1000;  // 2 s of the 100 MHz realtime counter
 };
 
 namespace {
@@ -310,6 +311,13 @@ int mk_set_timing(mk_handle* h, int64_t* stamps) {
   return MK_OK;
 }
 
+int mk_set_watchdog(mk_handle* h, int64_t ticks) {
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  if (ticks < 1) return fail(MK_ERR_INVALID_ARG, "watchdog ticks must be >= 1");
+  h->watchdog_ticks = ticks;
+  return MK_OK;
+}
+
 int mk_get_info(const mk_handle* h, mk_info* info) {
   if (!h || !info) return fail(MK_ERR_INVALID_ARG, "NULL argument");
   info->n_cu = h->n_cu;
@@ -376,7 +384,7 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
     p.ring_tiles = h->ring_tiles;
     p.x_bytes = h->x_bytes;
     p.barriers = h->barriers;
-    p.timeout_ticks = 200LL * 1000 * 1000;  // 2 s of the 100 MHz realtime counter
+    p.timeout_ticks = h->watchdog_ticks;
     p.layers = h->d_layers;
     p.hidden_in = hidden_in + (size_t)p.row0 * c.d_model;
     p.hidden_out = hidden_out + (size_t)p.row0 * c.d_model;

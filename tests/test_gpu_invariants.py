@@ -251,6 +251,39 @@ def test_timing_stamps_fill_their_buffer_exactly(env, name, G, M):
         run.close()
 
 
+def test_watchdog_timeout_is_reported_and_the_handle_recovers(env):
+    """The device watchdog, forced from the host: with a limit of a few ticks
+    every grid-barrier poll gives up at once, every workgroup leaves the
+    kernel at its next barrier, and mk_sync returns MK_ERR_TIMEOUT and resets
+    the handle; back at the default limit, the next step equals a clean step
+    bit for bit (its KV rows are rewritten at the same positions)."""
+    import moe_layer_stack_amd as mk
+    from parity_util import GpuRun
+    from synth.workloads import ATTN92_B1
+    torch = env
+    w = ATTN92_B1
+    _say(f"watchdog {w.name} L=2")
+    st = _stack(w, 2)
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        good = run.step(hid, w.positions(0)).clone()
+        with pytest.raises(mk.MkError):
+            mk.mk_set_watchdog(run.h, 0)
+        mk.mk_set_watchdog(run.h, 2)
+        pos = torch.as_tensor(np.asarray(w.positions(0), dtype=np.int32), device="cuda")
+        out = torch.empty_like(hid)
+        mk.mk_decode_step(run.h, hid.data_ptr(), pos.data_ptr(), st.kv(), out.data_ptr(), 0)
+        rc = mk.mk_sync(run.h, 0)
+        assert rc == mk.MK_ERR_TIMEOUT, (rc, mk.mk_last_error())
+        mk.mk_set_watchdog(run.h, 200_000_000)
+        again = run.step(hid, w.positions(0))
+        assert torch.equal(again, good)
+        _say("watchdog: timeout reported, next step equal")
+    finally:
+        run.close()
+
+
 def test_batch8_row_equals_batch1(env):
     """Sequences are independent: row 0 of a batch-8 step equals the batch-1
     step of sequence 0 (same row, same position, same cache)."""
