@@ -257,6 +257,25 @@ def moe16_legs(torch, mk, steps, warmup):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name (first processor of /proc/cpuinfo) and the
+    number of processors the process may run on."""
+    name = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count()
+    return name, n
+
+
 def cpu_baseline(torch, st, w, n_layers_sample, threads=None):
     """The CPU oracle (as it stands) on the first layers of a batch-1 step:
     host copies of the touched tensors are made before the timer starts.
@@ -288,7 +307,9 @@ def cpu_baseline(torch, st, w, n_layers_sample, threads=None):
         oracle.set_threads(all_threads)
     per_layer = t_compute / n_layers_sample
     step_s = per_layer * w.L
-    return dict(value=1.0 / step_s, unit="tokens/s", cores=used, kind="oracle",
+    model, n_avail = cpu_model()
+    return dict(value=1.0 / step_s, unit="tokens/s", cores=used, kind="oracle", cpu_model=model,
+                cpus_available=n_avail,
                 sample=f"first {n_layers_sample} of {w.L} layers of one batch-1 step (fp64 C oracle, OpenMP over "
                        f"output rows); compute time {t_compute:.1f} s, scaled by {w.L}/{n_layers_sample}")
 
@@ -356,6 +377,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the workload's 92)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed legs, one device copy of this size (counter calibration)")
+    ap.add_argument("--maps-out", default=None,
+                    help="after the teardown, copy /proc/self/maps to this file (to name the owner of an address "
+                         "in a crash report at exit)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic record from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -506,7 +530,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "attn92_b1", "layers": st.L, "d_model": w1.d, "experts": w1.E, "top_k": w1.k,
                    "shared_experts": w1.n_shared, "d_ff": w1.F, "q_heads": w1.H, "kv_heads": w1.G,
@@ -525,6 +549,17 @@ def main():
     if failed:
         out["failed_legs"] = failed
     print(json.dumps(out), flush=True)
+    # Release the device state before the interpreter exits: every handle is
+    # already destroyed by its leg; the stack's tensors and torch's cached
+    # blocks go here, after the last kernel has finished.
+    torch.cuda.synchronize()
+    del st
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    if args.maps_out:
+        with open("/proc/self/maps") as src, open(args.maps_out, "w") as dst:
+            dst.write(src.read())
+    log("teardown done")
 
 
 if __name__ == "__main__":

@@ -38,28 +38,19 @@ def env():
 
 
 def _check_step(torch, st, w, run, hid, pos):
-    from parity_util import assert_close, oracle_walk, tolerances
+    from parity_util import assert_close, assert_kv_rows, assert_routing_weights, oracle_walk, tolerances
     kv_before = [st.host_kv(l) for l in range(st.L)]
     out = run.step(hid, pos)
     torch.cuda.synchronize()
-    ids, wts, _ = run.trace()
-    ref, rep = oracle_walk(st, hid.cpu().numpy(), pos, ids, rows_per_seq=run.cfg.rows_per_seq, kv_hosts=kv_before)
+    ids, wts, logits = run.trace()
+    rps = run.cfg.rows_per_seq
+    ref, rep = oracle_walk(st, hid.cpu().numpy(), pos, ids, rows_per_seq=rps, kv_hosts=kv_before)
     assert not rep["mismatch"], f"expert sets differ beyond the tie margin: {rep['mismatch'][:5]}"
     c = assert_close(out.cpu().numpy(), ref, tolerances(w), f"{w.name} positions {pos}")
-    for l in range(st.L):
-        for r in range(run.M):
-            assert abs(float(wts[l, r].sum()) - 1.0) < 1e-5
-            if set(ids[l, r]) == set(rep["oracle_ids"][l][r]):
-                go = {int(e): float(x) for e, x in zip(ids[l, r], wts[l, r])}
-                oo = {int(e): float(x) for e, x in zip(rep["oracle_ids"][l][r], rep["oracle_w"][l][r])}
-                for e in go:
-                    assert abs(go[e] - oo[e]) < 2e-3, (l, r, e, go[e], oo[e])
-    # the new K/V rows landed at their positions (bf16 of the oracle's k, v up to rounding order)
-    kh, vh = st.host_kv(0)
-    for r, p in enumerate(pos):
-        s = r // run.cfg.rows_per_seq
-        assert (kh[s, :, p] != kv_before[0][0][s, :, p]).any(), f"row {r}: K at position {p} not written"
-        assert (vh[s, :, p] != kv_before[0][1][s, :, p]).any(), f"row {r}: V at position {p} not written"
+    assert_routing_weights(ids, wts, logits, rep, run.M, st.L, what=f"{w.name} positions {pos}")
+    # the new K/V rows at their positions, every layer, row and kv head: the
+    # oracle's bf16 rows within one bf16 step
+    c.update(assert_kv_rows(st, rep, pos, rps, what=f"{w.name} positions {pos}"))
     _say(f"{w.name} positions {pos}: {c} forced={rep['forced']}")
     return c
 

@@ -359,34 +359,67 @@ def test_moe16_feedback_steps(env):
         run.close()
 
 
-@pytest.mark.timeout(900)
-def test_attn92_full_depth_batch1_and_batch8_row(env):
-    """The benchmark's stack at full depth (92 layers): batch 1 against the
-    oracle, and row 0 of the batch-8 launch against batch 1."""
-    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+@pytest.mark.timeout(1500)
+def test_attn92_full_depth_batch1_batch8_and_verify8(env):
+    """The benchmark's stack at full depth (92 layers), every step against the
+    oracle walked over the same bytes: batch 1 (sequence 0), batch 8 (all 8
+    rows, each its own sequence), and a verify pass of 8 rows of sequence 0.
+    Every step's output, expert sets, routing weights and all the K/V rows it
+    appended (92 layers x rows x 8 kv heads) are checked; batch-8 row 0 also
+    equals the batch-1 step."""
+    from parity_util import (GpuRun, assert_close, assert_kv_rows, assert_routing_weights, oracle_walk,
+                             tolerances)
     from synth.workloads import ATTN92_B8
     torch = env
     w8 = ATTN92_B8
+    tol = tolerances(w8)
     _say(f"full depth {w8.name} L={w8.L}")
     st = _stack(w8)
-    kv0 = [tuple(x[:1].copy() for x in st.host_kv(l)) for l in range(st.L)]  # sequence 0
+
+    def walk(tag, hid, pos, ids, rps, kv_hosts):
+        def progress(l):
+            if l % 23 == 0:
+                _say(f"full depth {tag}: oracle at layer {l}")
+        return oracle_walk(st, hid, pos, ids, rows_per_seq=rps, kv_hosts=kv_hosts, progress=progress)
+
+    def check(tag, out, hid, pos, run, rps, kv_hosts):
+        ids, wts, logits = run.trace()
+        ref, rep = walk(tag, hid, pos, ids, rps, kv_hosts)
+        assert not rep["mismatch"], (tag, rep["mismatch"][:3])
+        c = assert_close(out.cpu().numpy(), ref, tol, f"full depth {tag}")
+        assert_routing_weights(ids, wts, logits, rep, run.M, st.L, what=tag)
+        c.update(assert_kv_rows(st, rep, pos, rps, what=f"full depth {tag}"))
+        _say(f"full depth {tag} {c} forced={rep['forced']}")
+
     hid = st.hidden(0)
     pos = w8.positions(0)
+    # batch 1: sequence 0
+    kv0 = [tuple(x[:1].copy() for x in st.host_kv(l)) for l in range(st.L)]
     r1 = GpuRun(st, rows=1, rows_per_seq=1)
     try:
         o1 = r1.step(hid[:1].contiguous(), pos[:1]).clone()
-        ids1, _, _ = r1.trace()
+        check("batch 1", o1, hid[:1].cpu().numpy(), pos[:1], r1, 1, kv0)
     finally:
         r1.close()
-    _say("full depth: oracle walk (92 layers)")
-    ref, rep = oracle_walk(st, hid[:1].cpu().numpy(), pos[:1], ids1, kv_hosts=kv0)
-    assert not rep["mismatch"], rep["mismatch"][:3]
-    c = assert_close(o1.cpu().numpy(), ref, tolerances(w8), "full depth batch 1")
-    _say(f"full depth batch 1 {c} forced={rep['forced']}")
+    del kv0
+    # batch 8: 8 sequences, one row each, over the cache as it stands now
+    kv8 = [st.host_kv(l) for l in range(st.L)]
     r8 = GpuRun(st)
     try:
         o8 = r8.step(hid, pos).clone()
+        check("batch 8", o8, hid.cpu().numpy(), pos, r8, 1, kv8)
     finally:
         r8.close()
-    assert_close(o8[:1].cpu().numpy(), o1.cpu().numpy(), tolerances(w8), "full depth batch-8 row 0")
-    assert bool(torch.isfinite(o8).all())
+    del kv8
+    assert_close(o8[:1].cpu().numpy(), o1.cpu().numpy(), tol, "full depth batch-8 row 0")
+    # verify: 8 rows of sequence 0 at positions past .. past+7 (the first of
+    # them overwrites the batch steps' row), causal among the drafts
+    pv = [w8.past + r for r in range(8)]
+    kvv = [tuple(x[:1].copy() for x in st.host_kv(l)) for l in range(st.L)]
+    rv = GpuRun(st, rows=8, rows_per_seq=8)
+    try:
+        hv = st.hidden(1)
+        ov = rv.step(hv, pv).clone()
+        check("verify 1 x 8", ov, hv.cpu().numpy(), pv, rv, 8, kvv)
+    finally:
+        rv.close()

@@ -22,7 +22,7 @@ def env():
 
 
 def _run_and_check(env, w, n_layers=None, step=0, check_kv=True):
-    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+    from parity_util import GpuRun, assert_close, assert_kv_rows, assert_routing_weights, oracle_walk, tolerances
     from synth.stack import DeviceStack
     torch = env
     _say(f"{w.name} L={n_layers or w.L} M={w.M} rps={w.rows_per_seq}")
@@ -38,25 +38,11 @@ def _run_and_check(env, w, n_layers=None, step=0, check_kv=True):
         ref, rep = oracle_walk(st, hid.cpu().numpy(), pos, ids, rows_per_seq=w.rows_per_seq, kv_hosts=kv_before)
         assert not rep["mismatch"], f"expert sets differ beyond the tie margin: {rep['mismatch'][:5]}"
         c = assert_close(out.cpu().numpy(), ref, tolerances(w), w.name)
-        # routing weights of rows whose set matched
-        for l in range(st.L):
-            for r in range(w.M):
-                if set(ids[l, r]) == set(rep["oracle_ids"][l][r]):
-                    go = {int(e): float(x) for e, x in zip(ids[l, r], wts[l, r])}
-                    oo = {int(e): float(x) for e, x in zip(rep["oracle_ids"][l][r], rep["oracle_w"][l][r])}
-                    for e in go:
-                        assert abs(go[e] - oo[e]) < 2e-3, (l, r, e, go[e], oo[e])
-                    assert abs(sum(go.values()) - 1.0) < 1e-5
+        assert_routing_weights(ids, wts, logits, rep, w.M, st.L, what=w.name)
         if w.has_attn and check_kv:
-            # the rows this step wrote equal bf16(oracle) up to one bf16 step
-            import oracle
-            from parity_util import dims_of, oracle_layer
-            for l in (0, st.L - 1):
-                kh, vh = st.host_kv(l)
-                for r, p in enumerate(pos):
-                    s = r // w.rows_per_seq
-                    kd = (kh[s, :, p].astype(np.int32) - kv_before[l][0][s, :, p].astype(np.int32))
-                    assert kd.any(), "new K row not written"
+            # every row this step appended (each layer, row and kv head) is
+            # the oracle's bf16 row within one bf16 step
+            c.update(assert_kv_rows(st, rep, pos, w.rows_per_seq, what=w.name))
         _say(f"{w.name} ok {c} forced={rep['forced']}")
         return out, ids
     finally:

@@ -29,7 +29,7 @@ def env():
 
 
 def test_rejected_drafts_do_not_reach_the_next_step(env):
-    from parity_util import GpuRun, assert_close, oracle_walk, tolerances
+    from parity_util import GpuRun, assert_close, assert_kv_rows, oracle_walk, tolerances
     from synth.stack import DeviceStack
     from synth.workloads import VERIFY92_M8
     torch = env
@@ -41,8 +41,19 @@ def test_rejected_drafts_do_not_reach_the_next_step(env):
         accepted = 2  # drafts accepted in step 1: tokens p0 .. p0+2 stay, p0+3 .. p0+7 are rolled back
         p1 = p0 + accepted + 1
         pristine = [(st.kc[l, 0].clone(), st.vc[l, 0].clone()) for l in range(st.L)]
+        kv0 = [st.host_kv(l) for l in range(st.L)]
+        pos1 = [p0 + r for r in range(8)]
+        hid1 = st.hidden(0)
         _say(f"{w.name} L=2 step 1 at {p0}..{p0 + 7}")
-        run.step(st.hidden(0), [p0 + r for r in range(8)])
+        out1 = run.step(hid1, pos1).clone()
+        ids1, _, _ = run.trace()
+        # step 1 against the oracle, and the 8 rows it appended (all of them,
+        # the drafts to be rejected included) before anything reuses the cache
+        ref1, rep1 = oracle_walk(st, hid1.cpu().numpy(), pos1, ids1, rows_per_seq=8, kv_hosts=kv0)
+        assert not rep1["mismatch"], rep1["mismatch"][:5]
+        c1 = assert_close(out1.cpu().numpy(), ref1, tolerances(w), "verify step 1")
+        c1.update(assert_kv_rows(st, rep1, pos1, 8, what="verify step 1"))
+        _say(f"{w.name} step 1 ok {c1}")
         after1 = [(st.kc[l, 0].clone(), st.vc[l, 0].clone()) for l in range(st.L)]
         kv_hosts = [st.host_kv(l) for l in range(st.L)]
         pos2 = [p1 + r for r in range(8)]
@@ -64,6 +75,8 @@ def test_rejected_drafts_do_not_reach_the_next_step(env):
         ref, rep = oracle_walk(st, hid2.cpu().numpy(), pos2, ids_a, rows_per_seq=8, kv_hosts=kv_hosts)
         assert not rep["mismatch"], rep["mismatch"][:5]
         c = assert_close(out_a.cpu().numpy(), ref, tolerances(w), "step after rollback")
+        # run b rewrote the same rows from the same inputs
+        c.update(assert_kv_rows(st, rep, pos2, 8, what="step after rollback"))
         _say(f"{w.name} rollback ok {c}")
     finally:
         run.close()
