@@ -177,6 +177,30 @@ int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* position
 int mk_decode_step_phased(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
                           float* hidden_out, void* stream);
 
+/* Size of the fixed device array that mk_decode_step_noalloc uses as its
+ * workspace: one per device, held from the library's load until the process
+ * ends. */
+#define MK_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* mk_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same step, bit for bit, with the step's workspace (activations and
+ * barrier counters) in a fixed array of MK_NOALLOC_SCRATCH_BYTES inside the
+ * library instead of the handle's workspace.  The call allocates nothing; the
+ * array's device address is taken once per device by the first mk_create on
+ * that device.  Arguments, layouts and ownership as mk_decode_step.  Errors:
+ * as mk_decode_step, and UNSUPPORTED when the handle's workspace
+ * (mk_info.workspace_bytes without its barrier block and pointer table) does
+ * not fit the array (about 64 MiB: e.g. a 16-layer MoE-only stack, or an
+ * attention stack of up to ~50 layers at one row; not the 92-layer stack).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (nothing a step reads depends on them): calls that overlap
+ * on one device (two streams or threads, any handles) race and must not be
+ * made.  Device-side errors are reported and cleared by the next mk_sync of
+ * the same handle, which then clears the whole array. */
+int mk_decode_step_noalloc(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+                           float* hidden_out, void* stream);
+
 /* Free the workspace and the handle.  NULL is accepted. */
 int mk_destroy(mk_handle* h);
 

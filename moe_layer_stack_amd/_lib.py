@@ -17,8 +17,9 @@ MK_ERR_HIP = -4
 MK_ERR_TIMEOUT = -5
 MK_F32, MK_BF16 = 0, 1
 
-EXPORTS = ("mk_create", "mk_decode_step", "mk_decode_step_phased", "mk_destroy", "mk_sync", "mk_set_trace", "mk_set_timing",
-           "mk_set_watchdog", "mk_get_info", "mk_strerror", "mk_last_error")
+EXPORTS = ("mk_create", "mk_decode_step", "mk_decode_step_phased", "mk_decode_step_noalloc", "mk_destroy", "mk_sync",
+           "mk_set_trace", "mk_set_timing", "mk_set_watchdog", "mk_get_info", "mk_strerror", "mk_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MK_NOALLOC_SCRATCH_BYTES
 
 
 class MkError(RuntimeError):
@@ -64,6 +65,7 @@ def lib():
         L.mk_decode_step.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(mk_kv_cache), C.c_void_p,
                                      C.c_void_p]
         L.mk_decode_step_phased.argtypes = L.mk_decode_step.argtypes
+        L.mk_decode_step_noalloc.argtypes = L.mk_decode_step.argtypes
         L.mk_destroy.argtypes = [C.c_void_p]
         L.mk_sync.argtypes = [C.c_void_p, C.c_void_p]
         L.mk_set_trace.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
@@ -74,8 +76,8 @@ def lib():
         L.mk_strerror.restype = C.c_char_p
         L.mk_last_error.argtypes = []
         L.mk_last_error.restype = C.c_char_p
-        for f in ("mk_create", "mk_decode_step", "mk_decode_step_phased", "mk_destroy", "mk_sync", "mk_set_trace",
-                  "mk_set_timing", "mk_set_watchdog", "mk_get_info"):
+        for f in ("mk_create", "mk_decode_step", "mk_decode_step_phased", "mk_decode_step_noalloc", "mk_destroy",
+                  "mk_sync", "mk_set_trace", "mk_set_timing", "mk_set_watchdog", "mk_get_info"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -113,6 +115,12 @@ def mk_decode_step_phased(h, hidden_in: int, positions: int, kv, hidden_out: int
     kvp = C.byref(kv) if kv is not None else None
     return _check(lib().mk_decode_step_phased(h, C.c_void_p(hidden_in), C.c_void_p(positions), kvp,
                                               C.c_void_p(hidden_out), C.c_void_p(stream) if stream else None))
+
+
+def mk_decode_step_noalloc(h, hidden_in: int, positions: int, kv, hidden_out: int, stream: int = 0) -> int:
+    kvp = C.byref(kv) if kv is not None else None
+    return _check(lib().mk_decode_step_noalloc(h, C.c_void_p(hidden_in), C.c_void_p(positions), kvp,
+                                               C.c_void_p(hidden_out), C.c_void_p(stream) if stream else None))
 
 
 def mk_destroy(h) -> int:

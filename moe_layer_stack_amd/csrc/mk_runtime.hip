@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -45,6 +46,44 @@ int launch_rows(const mk_config& c) { return c.rows < mk::kMaxRows ? c.rows : mk
 
 }  // namespace
 
+// ---- the workspace of mk_decode_step_noalloc
+//
+// A fixed device array in place of a handle's workspace, for callers that
+// cannot allocate: the barrier block first, then the activation workspace.
+// Every device that loads the library holds its own copy until the process
+// ends.  In host code `scratch` is only a stand-in for the symbol: the device
+// address of each device's copy comes from hipGetSymbolAddress, taken once
+// per device (at the first mk_create on that device, with it current) and
+// kept in g_scratch[device]; kernels get that address, never the symbol.
+static __device__ __align__(256) char scratch[MK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchSync = (SyncLayout::kWords * 4 + 255) & ~(size_t)255;  // barrier block, 256-byte aligned
+constexpr size_t kScratchAct = MK_NOALLOC_SCRATCH_BYTES - kScratchSync;          // activation workspace
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kScratchDevices] = {};
+
+// Once per device, with that device current: the device address of its copy
+// of `scratch`, zeroed (barrier counters and launch tags start at zero).
+// Returns MK_OK or an error status.
+int scratch_setup(int dev) {
+  if (dev < 0 || dev >= kScratchDevices) return MK_OK;  // mk_decode_step_noalloc then refuses this device
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return MK_OK;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) return fail(MK_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+  e = hipMemset(ptr, 0, MK_NOALLOC_SCRATCH_BYTES);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(MK_ERR_HIP, "clearing the no-allocation workspace failed: %s", hipGetErrorString(e));
+  g_scratch[dev] = static_cast<char*>(ptr);
+  return MK_OK;
+}
+
+}  // namespace
+
 struct mk_handle {
   mk_config cfg;
   int device;
@@ -65,6 +104,7 @@ struct mk_handle {
   float* t_logits = nullptr;
   int64_t* stamps = nullptr;
   long long watchdog_ticks = 200LL * 1000 * 1000;  // 2 s of the 100 MHz realtime counter
+  bool last_scratch = false;  // the last step ran in the no-allocation workspace
 };
 
 namespace {
@@ -165,6 +205,8 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
     return fail(MK_ERR_DEVICE, "device has %zu bytes of LDS per CU, need %d", prop.maxSharedMemoryPerMultiProcessor,
                 mk::kLdsTotal);
 
+  rc = scratch_setup(dev);  // the no-allocation entry point's workspace on this device
+  if (rc) return rc;
   mk_handle* h = new (std::nothrow) mk_handle();
   if (!h) return fail(MK_ERR_HIP, "out of host memory");
   h->cfg = c;
@@ -344,8 +386,9 @@ int launch_status(int e) {
 
 // One step: per group of up to kMaxRows rows, either one launch of the
 // persistent kernel or (phased) one launch per phase of every layer.
+// act, sync: the step's workspace (the handle's, or the no-allocation array)
 int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
-             float* hidden_out, void* stream, bool phased) {
+             float* hidden_out, void* stream, bool phased, char* act, unsigned* sync) {
   if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
   if (!hidden_in || !hidden_out || !positions) return fail(MK_ERR_INVALID_ARG, "NULL device pointer");
   const mk_config& c = h->cfg;
@@ -391,9 +434,9 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
     p.positions = positions + p.row0;
     p.kcache = c.has_attn ? static_cast<uint16_t*>(kv->k) : nullptr;
     p.vcache = c.has_attn ? static_cast<uint16_t*>(kv->v) : nullptr;
-    p.act = h->d_act;
+    p.act = act;
     p.al = h->al;
-    p.sync = h->d_sync;
+    p.sync = sync;
     p.t_ids = h->t_ids; p.t_w = h->t_w; p.t_logits = h->t_logits;
     if (!phased) {
       p.stamps = reinterpret_cast<long long*>(h->stamps);
@@ -424,28 +467,57 @@ extern "C" {
 
 int mk_decode_step(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
                    float* hidden_out, void* stream) {
-  return run_step(h, hidden_in, positions, kv, hidden_out, stream, false);
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  const int rc = run_step(h, hidden_in, positions, kv, hidden_out, stream, false, h->d_act, h->d_sync);
+  if (rc == MK_OK) h->last_scratch = false;
+  return rc;
 }
 
 int mk_decode_step_phased(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
                           float* hidden_out, void* stream) {
-  return run_step(h, hidden_in, positions, kv, hidden_out, stream, true);
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  const int rc = run_step(h, hidden_in, positions, kv, hidden_out, stream, true, h->d_act, h->d_sync);
+  if (rc == MK_OK) h->last_scratch = false;
+  return rc;
+}
+
+int mk_decode_step_noalloc(mk_handle* h, const float* hidden_in, const int32_t* positions, const mk_kv_cache* kv,
+                           float* hidden_out, void* stream) {
+  if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
+  if (h->act_bytes > kScratchAct)
+    return fail(MK_ERR_UNSUPPORTED, "the step needs %zu bytes of workspace; the no-allocation workspace holds %zu",
+                h->act_bytes, kScratchAct);
+  const int dev = h->device;
+  char* base = (dev >= 0 && dev < kScratchDevices) ? g_scratch[dev] : nullptr;  // set once per device by mk_create
+  if (!base) return fail(MK_ERR_DEVICE, "no no-allocation workspace on device %d", dev);
+  const int rc = run_step(h, hidden_in, positions, kv, hidden_out, stream, false, base + kScratchSync,
+                          reinterpret_cast<unsigned*>(base));
+  if (rc == MK_OK) h->last_scratch = true;
+  return rc;
 }
 
 int mk_sync(mk_handle* h, void* stream) {
   if (!h) return fail(MK_ERR_INVALID_ARG, "handle is NULL");
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MK_ERR_HIP, "stream synchronize failed: %s", hipGetErrorString(e));
+  // the barrier block of the workspace the last step ran in
+  char* scr = (h->last_scratch && h->device >= 0 && h->device < kScratchDevices) ? g_scratch[h->device] : nullptr;
+  unsigned* sync = scr ? reinterpret_cast<unsigned*>(scr) : h->d_sync;
   unsigned err = 0;
-  e = hipMemcpy(&err, h->d_sync + SyncLayout::kErr, 4, hipMemcpyDeviceToHost);
+  e = hipMemcpy(&err, sync + SyncLayout::kErr, 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(MK_ERR_HIP, "reading the device error flag failed: %s", hipGetErrorString(e));
   if (err == 0) return MK_OK;
   // reset barrier state, counters and the tag epoch so the handle can run
   // again; the workspace is cleared with it, so that no word tagged before
-  // the reset can carry a tag that the restarted epoch hands out again
-  if (hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess ||
-      hipMemset(h->d_act, 0, h->act_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+  // the reset can carry a tag that the restarted epoch hands out again (the
+  // whole no-allocation array: other handles' steps used it too)
+  if (scr) {
+    if (hipMemset(scr, 0, MK_NOALLOC_SCRATCH_BYTES) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+      return fail(MK_ERR_HIP, "resetting the no-allocation workspace failed");
+  } else if (hipMemset(h->d_sync, 0, SyncLayout::kWords * 4) != hipSuccess ||
+             hipMemset(h->d_act, 0, h->act_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     return fail(MK_ERR_HIP, "resetting the barrier state failed");
+  }
   if (err & mk::kErrTimeout) return fail(MK_ERR_TIMEOUT, "a grid barrier timed out (device flag 0x%x)", err);
   return fail(MK_ERR_INVALID_ARG, "a position was outside the cache or repeated within a sequence (flag 0x%x)", err);
 }
