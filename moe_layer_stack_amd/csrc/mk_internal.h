@@ -66,6 +66,7 @@ struct ActLayout {
   size_t y_s;     // [M][d]            shared-expert down projection
   size_t yp;      // [M][k][d]         routed down projections per top-k slot, weighted (rows > 1 only)
   size_t h2;      // [M][d]            layer output (next layer's input)
+  size_t umask;   // [n_groups][2] u32  expert-union masks of the row groups (group 0's workspace only)
   size_t stride;  // bytes per layer
 };
 
@@ -93,6 +94,12 @@ struct KParams {
   int q_per_task;            // query vectors per attention task: rps * (H / G) / q_groups
   int q_groups;              // attention tasks per (seq, kv head, split), each with its own queries
   int only_l, only_ph;       // one phase per launch: its layer and Phase; only_ph < 0: the whole step
+  // Row groups: n_groups groups of M rows (whole sequences) in one launch,
+  // each on vncu = n_cu / n_groups workgroups, 2^cpx_log2 of them per XCD;
+  // each group's activations at act + group * act_gstride (1, n_cu, 0, 0 for
+  // a launch of one group)
+  int n_groups, vncu, cpx_log2;
+  size_t act_gstride;
   // launch geometry / LDS carve-up
   int n_cu;
   int ring_tiles;

@@ -130,16 +130,28 @@ __device__ __forceinline__ void g2l(const void* g, unsigned lds_wave_base) {
 
 // Two 1 KiB chunks: g -> LDS base and g + 1024 -> base + 1024 (the
 // instruction offset applies to the global and the LDS address alike), one
-// M0 write for both.
-__device__ __forceinline__ void g2l2(const void* g, unsigned lds_wave_base) {
+// M0 write for both.  keep: without the nontemporal hint, so that the lines
+// stay in the caches for other workgroups that load the same tile (row
+// groups of one launch); nontemporal otherwise (every tile is read once).
+__device__ __forceinline__ void g2l2(const void* g, unsigned lds_wave_base, bool keep) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off nt\n\t"
-      "global_load_lds_dwordx4 %0, off offset:1024 nt"
-      :
-      : "v"(g), "s"(m0)
-      : "memory", "m0");
+  if (keep) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %0, off\n\t"
+        "global_load_lds_dwordx4 %0, off offset:1024"
+        :
+        : "v"(g), "s"(m0)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %0, off nt\n\t"
+        "global_load_lds_dwordx4 %0, off offset:1024 nt"
+        :
+        : "v"(g), "s"(m0)
+        : "memory", "m0");
+  }
 }
 
 // s_waitcnt with compiler memory-barrier semantics
@@ -268,14 +280,34 @@ typedef const __attribute__((address_space(4))) DevLayer* ConstLayers;
 __device__ __forceinline__ ConstLayers layer_tab(const KParams& p) { return (ConstLayers)p.layers; }
 
 
+// Row groups (several sequences of a verify pass in one launch).  Workgroup b
+// runs on XCD b % 8; group g's position c (0 <= c < vncu) is workgroup
+// 8 * (g * cpx + c % cpx) + c / cpx, cpx = vncu / 8, so position c of every
+// group sits on the same XCD and the groups' loads of one weight tile (the
+// same tile for position c of every group) meet in that XCD's L2.
+__device__ __forceinline__ int grp_of(const KParams& p) {
+  return p.n_groups == 1 ? 0 : (int)(blockIdx.x >> 3) >> p.cpx_log2;
+}
+__device__ __forceinline__ int vcu_of(const KParams& p) {
+  if (p.n_groups == 1) return (int)blockIdx.x;
+  return (int)((blockIdx.x & 7) << p.cpx_log2) + (int)((blockIdx.x >> 3) & ((1u << p.cpx_log2) - 1));
+}
+
 __device__ __forceinline__ const float* act_f(const KParams& p, int l, size_t off) {
-  return reinterpret_cast<const float*>(p.act + (size_t)l * p.al.stride + off);
+  return reinterpret_cast<const float*>(p.act + (size_t)grp_of(p) * p.act_gstride + (size_t)l * p.al.stride + off);
 }
 __device__ __forceinline__ float* act_w(const KParams& p, int l, size_t off) {
-  return reinterpret_cast<float*>(p.act + (size_t)l * p.al.stride + off);
+  return reinterpret_cast<float*>(p.act + (size_t)grp_of(p) * p.act_gstride + (size_t)l * p.al.stride + off);
+}
+// this group's rows of the step's input and output
+__device__ __forceinline__ const float* hidden_in_g(const KParams& p) {
+  return p.hidden_in + (size_t)grp_of(p) * p.M * p.d;
+}
+__device__ __forceinline__ float* hidden_out_g(const KParams& p) {
+  return p.hidden_out + (size_t)grp_of(p) * p.M * p.d;
 }
 __device__ __forceinline__ const float* layer_in(const KParams& p, int l) {
-  return l == 0 ? p.hidden_in : act_f(p, l - 1, p.al.h2);
+  return l == 0 ? hidden_in_g(p) : act_f(p, l - 1, p.al.h2);
 }
 // h1 of layer l: the attention block's output, or the layer input when the
 // stack has no attention
@@ -303,10 +335,11 @@ __device__ __forceinline__ QR divmod_small(int a, int b) {
   }
   return QR{q, r};
 }
-// balanced split of n items over the grid (blockIdx * n stays below 2^32)
-__device__ __forceinline__ void my_range(int n, int ncu, int& lo, int& hi) {
-  lo = (int)((blockIdx.x * (unsigned)n) / (unsigned)ncu);
-  hi = (int)(((blockIdx.x + 1) * (unsigned)n) / (unsigned)ncu);
+// balanced split of n items over the group's workgroups (c * n stays below 2^32)
+__device__ __forceinline__ void my_range(int n, const KParams& p, int& lo, int& hi) {
+  const unsigned c = (unsigned)vcu_of(p), ncu = (unsigned)p.vncu;
+  lo = (int)((c * (unsigned)n) / ncu);
+  hi = (int)(((c + 1) * (unsigned)n) / ncu);
 }
 
 // ------------------------------------------------------------------ phase plans
@@ -417,7 +450,7 @@ __device__ __forceinline__ Plan plan_qkv(const KParams& p, int l) {
   P.a0 = p.H * p.hd;
   P.a1 = p.G * p.hd;
   int lo, hi;
-  my_range((P.a0 + 2 * P.a1) / P.rpt, p.n_cu, lo, hi);
+  my_range((P.a0 + 2 * P.a1) / P.rpt, p, lo, hi);
   P.lo = lo;
   P.n = hi - lo;
   P.b0 = (const char*)Ly.wq;
@@ -431,8 +464,8 @@ __device__ __forceinline__ Plan plan_qkv(const KParams& p, int l) {
 // the 8 XCDs round-robin; tasks are numbered XCD by XCD, so the splits of one
 // (sequence, kv head), consecutive tasks, share an XCD when the split count
 // divides the CUs per XCD, and their partial records meet in that XCD's L2.
-__device__ __forceinline__ int attn_task(int ncu) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ int attn_task(const KParams& p) {
+  const int b = vcu_of(p), ncu = p.vncu;
   return (ncu & 7) ? b : (b & 7) * (ncu >> 3) + (b >> 3);
 }
 
@@ -444,7 +477,7 @@ __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int 
   Plan P{};
   P.kind = PK_ATTN;
   const int S = p.n_splits, QG = p.q_groups;
-  const int task = attn_task(p.n_cu);
+  const int task = attn_task(p);
   if (task >= p.n_seq * p.G * QG * S) return P;
   const int seq = task / (p.G * QG * S), g = (task / (QG * S)) % p.G, s = task % S;
   int maxpos = 0;
@@ -458,7 +491,8 @@ __device__ __forceinline__ Plan plan_attn(const KParams& p, const Misc* ms, int 
   P.n = 2 * (t_hi - t_lo);
   P.U = (tr && s == S - 1) ? 1 : 0;
   P.F = maxpos;
-  const size_t kv_base = ((((size_t)l * p.kv_seqs + p.seq0 + seq) * p.G + g) * (size_t)p.cap) * p.hd;
+  const size_t kv_base =
+      ((((size_t)l * p.kv_seqs + p.seq0 + (size_t)grp_of(p) * p.n_seq + seq) * p.G + g) * (size_t)p.cap) * p.hd;
   P.b0 = reinterpret_cast<const char*>(p.kcache + kv_base);
   P.b1 = reinterpret_cast<const char*>(p.vcache + kv_base);
   P.lo = task;
@@ -472,7 +506,7 @@ __device__ __forceinline__ Plan plan_wo(const KParams& p, int l) {
   P.lrb = ilog2(p.H * p.hd * (int)sizeof(WT));
   P.rpt = kTileBytes >> P.lrb;
   int lo, hi;
-  my_range(p.d / P.rpt, p.n_cu, lo, hi);
+  my_range(p.d / P.rpt, p, lo, hi);
   P.lo = lo;
   P.n = hi - lo;
   P.b0 = (const char*)layer_tab(p)[l].wo;
@@ -494,7 +528,7 @@ __device__ __forceinline__ Plan plan_rs(const KParams& p, int l) {
   P.fb_per = p.F / P.rpt;
   const int npair = p.S * P.fb_per;
   int lo, hi;
-  my_range(nrt + 2 * npair, p.n_cu, lo, hi);
+  my_range(nrt + 2 * npair, p, lo, hi);
   const int r_lo = min(lo, nrt), r_hi = min(hi, nrt);
   auto ceil_half = [](int x) { return x <= 0 ? 0 : (x + 1) / 2; };
   const int pl = min(npair, ceil_half(lo - nrt)), ph = min(npair, ceil_half(hi - nrt));
@@ -523,7 +557,7 @@ __device__ __forceinline__ Plan plan_rg(const KParams& p, const Misc* ms, int l,
   P.F = p.F;
   P.S = p.S;
   int lo, hi;
-  my_range(p.S > 0 ? p.d / P.rpt : 0, p.n_cu, lo, hi);
+  my_range(p.S > 0 ? p.d / P.rpt : 0, p, lo, hi);
   P.lo = lo;
   P.nj = hi - lo;
   P.n1 = (hi - lo) * p.S;
@@ -531,7 +565,7 @@ __device__ __forceinline__ Plan plan_rg(const KParams& p, const Misc* ms, int l,
   P.n = P.n1;
   if (routed) {
     int l2, h2;
-    my_range(ms->n_uni * P.fb_per, p.n_cu, l2, h2);
+    my_range(ms->n_uni * P.fb_per, p, l2, h2);
     P.lo2 = l2;
     P.n += 2 * (h2 - l2);
   }
@@ -550,7 +584,7 @@ __device__ __forceinline__ Plan plan_down(const KParams& p, const Misc* ms, int 
   P.d = p.d;
   P.U = ms->n_uni;
   int lo, hi;
-  my_range(p.d / P.rpt, p.n_cu, lo, hi);
+  my_range(p.d / P.rpt, p, lo, hi);
   P.lo = lo;
   P.nj = hi - lo;
   P.n = (hi - lo) * P.U;
@@ -572,10 +606,10 @@ __device__ __forceinline__ Plan plan_down_a(const KParams& p, const Misc* ms, in
   P.U = ms->n_uni;
   P.nj = p.d / P.rpt;
   int lo, hi;
-  my_range(P.U * P.nj, p.n_cu, lo, hi);
+  my_range(P.U * P.nj, p, lo, hi);
   P.lo = lo;
   P.n = hi - lo;
-  my_range(P.nj, p.n_cu, lo, hi);
+  my_range(P.nj, p, lo, hi);
   P.lo2 = lo;
   P.n1 = hi - lo;
   P.b0 = (const char*)layer_tab(p)[l].w_down;
@@ -607,14 +641,14 @@ __device__ __forceinline__ Win build_win(const Plan& P, int w0, const Misc* ms, 
 }
 
 // issue this wave's quarter of tile j (of the window's plan) into `slot`
-__device__ __forceinline__ void issue_tile(const Win& w, int j, unsigned slot_lds, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(const Win& w, int j, unsigned slot_lds, int wave, int lane, bool keep) {
   const int idx = j - w.w0;
   const unsigned lo = __builtin_amdgcn_readlane(w.lo, idx);
   const unsigned hi = __builtin_amdgcn_readlane(w.hi, idx);
   const char* g = reinterpret_cast<const char*>(((unsigned long long)(hi & 0x07ffffffu) << 32) | lo);
   const int off0 = wave * 2048 + lane * 16;
   if ((hi >> 27) == 0) {  // a whole tile (the common case; wave-uniform)
-    g2l2(g + off0, slot_lds + wave * 2048);
+    g2l2(g + off0, slot_lds + wave * 2048, keep);
     return;
   }
   const int valid = kTileBytes - (int)((hi >> 27) << 8);
@@ -641,6 +675,7 @@ struct Stream {
   Win wc, wn;     // address windows of the current and the next plan
   int islot;      // ring slot of tile `issued`
   unsigned ring_lds;
+  bool keep;      // tile loads keep their lines in the caches (row groups of one launch)
   __device__ __forceinline__ void mark(int k) const {
     if (ts && threadIdx.x == 0) ts[k] = wall_clock64();
   }
@@ -660,11 +695,11 @@ struct Stream {
       islot = islot == kRing - 1 ? 0 : islot + 1;
       if (issued < cur.n) {
         if ((unsigned)(issued - wc.w0) >= 64u) wc = build_win<KC>(cur, issued, sm.misc, lane);
-        issue_tile(wc, issued, s, wave, lane);
+        issue_tile(wc, issued, s, wave, lane, keep);
       } else {
         const int j = issued - cur.n;
         if ((unsigned)(j - wn.w0) >= 64u) wn = build_win<KN>(nxt, j, sm.misc, lane);
-        issue_tile(wn, j, s, wave, lane);
+        issue_tile(wn, j, s, wave, lane, keep);
       }
     }
   }
@@ -1417,7 +1452,7 @@ __device__ __forceinline__ void phase_attn_dec(const KParams& p, Smem sm, int l,
   uint16_t* nkb = reinterpret_cast<uint16_t*>(sm.xs + kHeadF);  // [rps][128] bf16 copies
   uint16_t* nvb = nkb + kMaxRows * 128;
   static_assert(kHeadF * 4 + 2 * kMaxRows * 128 * 2 <= kXsBytes, "attention scratch exceeds the x region");
-  const int task = attn_task(p.n_cu);
+  const int task = attn_task(p);
   const bool active = task < ntask;
   const int seq = active ? task / (p.G * QG * S) : 0, g = active ? (task / (QG * S)) % p.G : 0;
   const int qg = active ? (task / S) % QG : 0, s = active ? task % S : 0;
@@ -1811,13 +1846,14 @@ __device__ __forceinline__ void route_tables(const KParams& p, Smem sm, int l) {
     ms->umask[u] = m;
   }
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (vcu_of(p) == 0) {  // one workgroup of each row group
+    const int row0 = p.row0 + grp_of(p) * M;
     for (int i = threadIdx.x; i < M * k; i += kThreads) {
-      if (p.t_ids) p.t_ids[((size_t)l * p.Mt + p.row0) * k + i] = ms->ids[i];
-      if (p.t_w) p.t_w[((size_t)l * p.Mt + p.row0) * k + i] = ms->wts[i];
+      if (p.t_ids) p.t_ids[((size_t)l * p.Mt + row0) * k + i] = ms->ids[i];
+      if (p.t_w) p.t_w[((size_t)l * p.Mt + row0) * k + i] = ms->wts[i];
     }
     if (p.t_logits)
-      for (int i = threadIdx.x; i < M * E; i += kThreads) p.t_logits[((size_t)l * p.Mt + p.row0) * E + i] = logits[i];
+      for (int i = threadIdx.x; i < M * E; i += kThreads) p.t_logits[((size_t)l * p.Mt + row0) * E + i] = logits[i];
   }
 }
 
@@ -1967,7 +2003,7 @@ __device__ __forceinline__ void phase_down(const KParams& p, Smem sm, int l, Str
   const float* h1 = layer_h1(p, l);
   const float* a_g = act_f(p, l, p.al.a);    // [M][k][F]
   const float* ys = act_f(p, l, p.al.y_s);   // [M][d]
-  float* h2 = (l == p.L - 1) ? p.hidden_out : act_w(p, l, p.al.h2);
+  float* h2 = (l == p.L - 1) ? hidden_out_g(p) : act_w(p, l, p.al.h2);
   const bool last_layer = (l == p.L - 1);
   const bool xl = (size_t)M * k * F * 4 <= (size_t)kXsBytes;
   if (xl) dma_to_lds((char*)sm.xs, (const char*)a_g, M * k * F * 4, wave, lane);
@@ -2138,7 +2174,7 @@ __device__ __forceinline__ void phase_down_b(const KParams& p, Smem sm, int l, i
   const int d = p.d, k = p.k, M = p.M;
   const float* yp = act_f(p, l, p.al.yp);
   const bool last_layer = (l == p.L - 1);
-  float* h2 = last_layer ? p.hidden_out : act_w(p, l, p.al.h2);
+  float* h2 = last_layer ? hidden_out_g(p) : act_w(p, l, p.al.h2);
   const float* res = res_slice(sm);
   for (int it = threadIdx.x; it < ncol * M; it += kThreads) {
     const int t = it / ncol, c = it - t * ncol;
@@ -2174,8 +2210,9 @@ __device__ __forceinline__ bool launch_setup(const KParams& p, Smem sm) {
   Misc* ms = sm.misc;
   if (threadIdx.x == 0) {
     int bad = 0;
+    const int* positions = p.positions + (size_t)grp_of(p) * p.M;
     for (int r = 0; r < p.M; ++r) {
-      const int pos = p.positions[r];
+      const int pos = positions[r];
       ms->pos[r] = pos;
       if (p.attn && (pos < 0 || pos >= p.cap)) bad |= kErrPosition;
     }
@@ -2211,6 +2248,51 @@ __device__ __forceinline__ bool launch_setup(const KParams& p, Smem sm) {
   return true;
 }
 
+// Row groups: the expert union of all groups of the launch.  Each group's
+// routing (route_rank, the same in all its workgroups) gives its own union;
+// one workgroup per group publishes it as a mask (write-once per launch),
+// and after the next grid barrier every workgroup replaces its union by the
+// union of all masks, in ascending expert order.  All groups then walk the
+// same routed tiles in the same order (a group's rows not routed to an
+// expert contribute nothing), so position c of every group loads the same
+// tile at about the same time and the copies meet in the XCD's L2.
+__device__ __forceinline__ void publish_union(const KParams& p, Smem sm, int l) {
+  if (vcu_of(p) != 0) return;
+  unsigned* um = reinterpret_cast<unsigned*>(p.act + (size_t)l * p.al.stride + p.al.umask) + 2 * grp_of(p);
+  const Misc* ms = sm.misc;
+  if (threadIdx.x < 64) {
+    const bool in = (int)threadIdx.x < ms->n_uni;
+    const int e = ms->uni[in ? threadIdx.x : 0];
+    unsigned long long m = 0;
+    // OR of the lanes' bits: one bit per union expert
+    const unsigned long long bit = in ? (1ull << e) : 0ull;
+    unsigned lo = (unsigned)bit, hi = (unsigned)(bit >> 32);
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      lo |= __shfl_xor(lo, sh);
+      hi |= __shfl_xor(hi, sh);
+    }
+    m = ((unsigned long long)hi << 32) | lo;
+    if (threadIdx.x == 0) {
+      st_dev_u(um, (unsigned)m);
+      st_dev_u(um + 1, (unsigned)(m >> 32));
+    }
+  }
+}
+__device__ __forceinline__ void merge_unions(const KParams& p, Smem sm, int l) {
+  const unsigned* um = reinterpret_cast<const unsigned*>(p.act + (size_t)l * p.al.stride + p.al.umask);
+  Misc* ms = sm.misc;
+  if (threadIdx.x < 64) {
+    const int e = threadIdx.x;
+    bool in = false;
+    for (int g = 0; g < p.n_groups; ++g) in |= ((um[2 * g + (e >> 5)] >> (e & 31)) & 1u) != 0;
+    in &= e < p.E;
+    const unsigned long long mm = __ballot(in);
+    if (in) ms->uni[__popcll(mm & ((1ull << e) - 1ull))] = e;
+    if (e == 0) ms->n_uni = __popcll(mm);
+  }
+  __syncthreads();
+}
+
 // WT: weight element type; MT: rows of the token group (1 or 8); QK: kind of
 // attention task, 1: at most 4 query vectors, 2: at most 16
 template <typename WT, int MT, int QK>
@@ -2224,7 +2306,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   unsigned b = 0;
   long long* stamp = p.stamps ? p.stamps + (size_t)blockIdx.x * 4 * (p.barriers + 1) : nullptr;
   XRegs<WT, MT> xr_moe;
-  Stream st{0, 0, stamp, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring)};
+  Stream st{0, 0, stamp, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring), p.n_groups > 1};
   const int wave = wave_id(), lane = threadIdx.x & 63;
   // phase i owns slots 4i..4i+3: start (after barrier i), tile loop start,
   // tile loop end, end (before barrier i+1)
@@ -2271,6 +2353,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
     {
       rg_stage(p, sm, l);
       route_rank(p, sm, l);
+      if (p.n_groups > 1) {  // all row groups stream the union of their experts
+        publish_union(p, sm, l);
+        MK_SYNC();
+        merge_unions(p, sm, l);
+      }
       cur = plan_rg<WT>(p, ms, l, true);  // same first tiles as the prefetched plan
       const Plan nxt = MT == 1 ? plan_down<WT>(p, ms, l) : plan_down_a<WT>(p, ms, l);
       // the routed tiles start streaming as soon as the union is known
@@ -2327,7 +2414,7 @@ __global__ void __launch_bounds__(kThreads, 1) phase_step_kernel(KParams kp) {
   const int l = p.only_l;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const Plan none{};
-  Stream st{0, 0, nullptr, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring)};
+  Stream st{0, 0, nullptr, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring), false};
   XRegs<WT, MT> xr;
   switch (p.only_ph) {
     case PH_QKV:
@@ -2385,7 +2472,8 @@ constexpr int kKernelKinds = 6;
 static int mk_pick(const mk::KParams& p, bool phased, const void** fn, int* idx) {
   using namespace mk;
   if (p.M < 1 || p.M > kMaxRows) return -2;
-  if (p.attn && p.n_seq * p.G * p.q_groups * p.n_splits > p.n_cu) return -2;
+  if (p.attn && p.n_seq * p.G * p.q_groups * p.n_splits > p.vncu) return -2;
+  if (p.n_groups < 1 || p.n_groups * p.vncu != p.n_cu || (p.n_groups > 1 && p.vncu != 8 << p.cpx_log2)) return -2;
   const int Q = p.attn ? p.q_per_task : 0;
   const bool one = p.M == 1;
   // instantiations: weight dtype x token group (1 or 8) x attention task

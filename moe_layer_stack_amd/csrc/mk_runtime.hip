@@ -88,6 +88,9 @@ struct mk_handle {
   mk_config cfg;
   int device;
   int n_cu;
+  int n_groups;   // row groups of kMaxRows rows run in one launch (1: a launch per group of rows)
+  int vncu;       // workgroups per row group
+  int cpx_log2;   // log2 of a row group's workgroups per XCD
   int n_splits;
   int q_groups;  // attention tasks per (sequence, kv head, split)
   int q_task;    // query vectors per attention task
@@ -214,6 +217,22 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   h->n_cu = prop.multiProcessorCount;
   const int M = launch_rows(c);
   const int n_seq = M / c.rows_per_seq;
+  // A step of more than kMaxRows rows runs its groups of kMaxRows rows in one
+  // launch when the CUs split into equal groups with the same power-of-two
+  // number on every XCD (workgroups are dealt to the 8 XCDs round-robin);
+  // otherwise as one launch per group.
+  h->n_groups = 1;
+  h->vncu = h->n_cu;
+  h->cpx_log2 = 0;
+  if (c.rows > M) {
+    const int ng = c.rows / M;
+    const int per = h->n_cu / ng;
+    if (h->n_cu % (8 * ng) == 0 && ((per / 8) & (per / 8 - 1)) == 0) {
+      h->n_groups = ng;
+      h->vncu = per;
+      while ((8 << h->cpx_log2) < per) ++h->cpx_log2;
+    }
+  }
   const int H = c.has_attn ? c.n_heads : 0, G = c.has_attn ? c.n_kv_heads : 0, hd = c.has_attn ? c.head_dim : 0;
   h->n_splits = 1;
   h->q_groups = 1;
@@ -230,12 +249,12 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
                   "groups of at most %d", Qall, mk::kMaxQTask);
     }
     h->q_task = Qall / h->q_groups;
-    if (n_seq * G * h->q_groups > h->n_cu) {  // one attention task per CU at least
+    if (n_seq * G * h->q_groups > h->vncu) {  // one attention task per CU at least
       delete h;
       return fail(MK_ERR_UNSUPPORTED, "%d sequences x %d kv heads x %d query groups exceed the %d CUs", n_seq, G,
-                  h->q_groups, h->n_cu);
+                  h->q_groups, h->vncu);
     }
-    int s = h->n_cu / (n_seq * G * h->q_groups);
+    int s = h->vncu / (n_seq * G * h->q_groups);
     if (s < 1) s = 1;
     int maxs = (c.kv_capacity + mk::kAttnTile - 1) / mk::kAttnTile;
     if (s > maxs) s = maxs;
@@ -262,7 +281,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
     auto cols = [&](int row_elems) {
       const int rpt = mk::kTileBytes / (row_elems * esz);
       const int units = c.d_model / rpt;
-      return ((units + h->n_cu - 1) / h->n_cu) * rpt;
+      return ((units + h->vncu - 1) / h->vncu) * rpt;
     };
     int ncol = cols(c.d_ff);
     if (c.has_attn && cols(c.n_heads * c.head_dim) > ncol) ncol = cols(c.n_heads * c.head_dim);
@@ -273,7 +292,9 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   }
   // several rows: the routed down projection runs in two phases (expert-major
   // products, then the per-column sum), one more barrier per layer
-  h->barriers = c.n_layers * ((c.has_attn ? 6 : 3) + (M > 1 ? 1 : 0)) - 1;
+  // and row groups in one launch meet at one more barrier per layer, where
+  // they exchange their expert unions
+  h->barriers = c.n_layers * ((c.has_attn ? 6 : 3) + (M > 1 ? 1 : 0) + (h->n_groups > 1 ? 1 : 0)) - 1;
   // LDS: fixed carve-up (ring, x staging, per-row partial sums, misc)
   h->x_bytes = mk::kXsBytes;
   h->ring_tiles = mk::kRing;
@@ -297,9 +318,10 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   al.y_s = take((size_t)M * d * 4);
   al.yp = take(M > 1 ? (size_t)M * k * d * 4 : 0);
   al.h2 = take((size_t)M * d * 4);
+  al.umask = take((size_t)h->n_groups * 8);
   al.stride = align256(off);
   h->al = al;
-  h->act_bytes = al.stride * c.n_layers;
+  h->act_bytes = al.stride * c.n_layers * h->n_groups;  // a workspace per row group
 
   auto cleanup = [&]() {
     if (h->d_layers) (void)hipFree(h->d_layers);
@@ -407,7 +429,10 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return fail(MK_ERR_INVALID_ARG, "current device differs from the handle's device");
   const int Mg = launch_rows(c);
-  const int n_launch = c.rows / Mg;
+  // the persistent kernel runs all row groups in one launch when the handle
+  // allows it; the phase launches take one row group at a time
+  const bool grouped = !phased && h->n_groups > 1;
+  const int n_launch = grouped ? 1 : c.rows / Mg;
   for (int gi = 0; gi < n_launch; ++gi) {
     KParams p{};
     p.L = c.n_layers; p.d = c.d_model; p.E = c.n_experts; p.k = c.top_k; p.S = c.n_shared; p.F = c.d_ff;
@@ -424,9 +449,15 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
     p.q_per_task = h->q_task;
     p.q_groups = h->q_groups;
     p.n_cu = h->n_cu;
+    p.n_groups = grouped ? h->n_groups : 1;
+    p.vncu = grouped ? h->vncu : h->n_cu;
+    p.cpx_log2 = grouped ? h->cpx_log2 : 0;
+    p.act_gstride = grouped ? h->al.stride * c.n_layers : 0;
     p.ring_tiles = h->ring_tiles;
     p.x_bytes = h->x_bytes;
-    p.barriers = h->barriers;
+    // barriers of this launch (the row groups' union exchange only when grouped)
+    p.barriers = grouped || h->n_groups == 1 ? h->barriers
+                                             : c.n_layers * ((c.has_attn ? 6 : 3) + (Mg > 1 ? 1 : 0)) - 1;
     p.timeout_ticks = h->watchdog_ticks;
     p.layers = h->d_layers;
     p.hidden_in = hidden_in + (size_t)p.row0 * c.d_model;
