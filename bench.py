@@ -131,7 +131,8 @@ def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush
     finite = bool(torch.isfinite(bufs[total % 2]).all().item())
     union_layers = [round(float(np.mean([unions[t][l] for t in range(warmup, total)])), 2) for l in range(st.L)]
     n_groups = max(1, M // 8)
-    launches = n_groups * (st.L * ((6 if w.has_attn else 3) + (1 if M > 1 else 0)) if phased else 1)
+    launches = (n_groups * st.L * ((6 if w.has_attn else 3) + (1 if M > 1 else 0)) if phased
+                else info.launches_per_step)
     return dict(M=M, ms_per_step=ms, ms_median=float(np.median(durs)), ms_p10=float(np.percentile(durs, 10)),
                 ms_p90=float(np.percentile(durs, 90)),
                 wall_ms_per_step=t_wall * 1e3 / steps, tok_s=M / (ms * 1e-3), bytes_per_step=float(np.mean(byts)),

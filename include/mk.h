@@ -105,14 +105,18 @@ typedef struct mk_config {
   int32_t head_dim;        /* hd = 128 */
   float rope_theta;        /* > 0 */
   int32_t rows;            /* M, 1..64, fixed per handle.  Above 8, a multiple of 8 with
-                              rows_per_seq dividing 8: the step then runs its rows/8
-                              groups of 8 rows (whole sequences) in one launch, each
-                              group on an equal share of the CUs, all groups streaming
-                              the same weight tiles in step so that each tile is read
-                              from HBM about once (the expert union is that of all
-                              rows).  Where the CUs do not split that way (a power-of-
-                              two number per group and XCD), as rows/8 launches of 8
-                              rows on the stream */
+                              rows_per_seq dividing 8.  With bf16 weights the step then
+                              runs its rows/8 groups of 8 rows (whole sequences) in one
+                              launch: each group on an equal share of the CUs for the
+                              attention block, the router and the shared expert (the
+                              groups stream the same weight tiles in step, so each tile
+                              is read from HBM about once), and the routed experts as
+                              tasks of one expert and at most 8 of the rows of all groups
+                              routed to it, spread over every CU (an expert chosen by n
+                              rows is streamed ceil(n/8) times).  With fp32 weights, or
+                              where the CUs do not split that way (a power-of-two number
+                              per group and XCD), as rows/8 launches of 8 rows on the
+                              stream */
   int32_t rows_per_seq;    /* 1 for decode; > 1 for a verify pass; divides M */
   int32_t kv_capacity;     /* positions per sequence in the cache (attention stacks) */
 } mk_config;
@@ -147,8 +151,10 @@ typedef struct mk_info {
   int32_t lds_bytes;         /* dynamic LDS per workgroup */
   int32_t barriers_per_step; /* grid barriers one launch executes (a step of row groups in
                                 one launch has one more per layer, where the groups
-                                exchange their expert unions) */
+                                publish their routing) */
   int32_t attn_splits;       /* KV splits per (sequence, kv head) */
+  int32_t launches_per_step; /* kernel launches of one mk_decode_step: 1, or rows/8 when the
+                                row groups run one launch each */
   int64_t workspace_bytes;   /* device memory owned by the handle */
 } mk_info;
 

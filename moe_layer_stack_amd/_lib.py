@@ -48,7 +48,8 @@ class mk_kv_cache(C.Structure):
 
 class mk_info(C.Structure):
     _fields_ = [("n_cu", C.c_int32), ("threads", C.c_int32), ("lds_bytes", C.c_int32),
-                ("barriers_per_step", C.c_int32), ("attn_splits", C.c_int32), ("workspace_bytes", C.c_int64)]
+                ("barriers_per_step", C.c_int32), ("attn_splits", C.c_int32), ("launches_per_step", C.c_int32),
+                ("workspace_bytes", C.c_int64)]
 
 
 _lib = None

@@ -14,6 +14,7 @@ constexpr int kChunk = 1024;            // one global_load_lds: 64 lanes x 16 B
 constexpr int kRing = 12;               // ring slots (tiles in flight per CU)
 constexpr int kSlotBytes = kTileBytes + 128;  // slot pitch: four neighbouring slots start in different LDS bank halves
 constexpr int kMaxRows = 8;             // M
+constexpr int kMaxGroups = 8;           // row groups of one launch (kMaxRows rows each)
 constexpr int kMaxExperts = 64;         // E (one lane per expert in top-k)
 constexpr int kMaxTopK = 8;
 constexpr int kMaxShared = 4;
@@ -66,7 +67,8 @@ struct ActLayout {
   size_t y_s;     // [M][d]            shared-expert down projection
   size_t yp;      // [M][k][d]         routed down projections per top-k slot, weighted (rows > 1 only)
   size_t h2;      // [M][d]            layer output (next layer's input)
-  size_t umask;   // [n_groups][2] u32  expert-union masks of the row groups (group 0's workspace only)
+  size_t rtab;    // [n_groups][M][k] i32 top-k ids, then [n_groups][M][k] fp32 weights: every row
+                  // group's routing (group 0's workspace only; row-group launches)
   size_t stride;  // bytes per layer
 };
 

@@ -190,6 +190,10 @@ static_assert(kRing == 12, "wait_tiles_ahead is written for a ring of 12 tiles")
 
 __device__ __forceinline__ int ilog2(int x) { return 31 - __builtin_clz(x); }
 
+// Tasks of a row-group launch: an expert's list of pairs is cut into pieces
+// of at most kMaxRows, so there are at most E + (rows * k) / kMaxRows.
+constexpr int kMaxTasks = kMaxExperts + kMaxGroups * kMaxTopK;
+
 // ------------------------------------------------------------------ LDS carve-up
 
 struct Misc {
@@ -208,6 +212,15 @@ struct Misc {
   unsigned umask[kMaxExperts];                 // union expert u: rows routed to it
   signed char uslot[kMaxExperts * kMaxRows];   // [u][t]: top-k slot of expert u in row t, or -1
   float rope[kMaxRows * 64 * 2];  // (cos, sin) per row and frequency (head_dim 128)
+  // Row-group launches: the routed work as tasks, each an expert and at most
+  // kMaxRows of the (row, top-k slot) pairs of all groups routed to it.
+  // tent: entries expert << 9 | row << 3 | slot (row = group * M + row in
+  // group), by expert, rows ascending; task t owns tent[tbeg[t] .. tbeg[t+1]).
+  unsigned short tent[kMaxGroups * kMaxRows * kMaxTopK];
+  unsigned short tbeg[kMaxTasks + 2];
+  int n_task;
+  float rinv_row[kMaxGroups * kMaxRows];  // 1/rms of h1 per row, set when a task's rows are loaded
+  float task_w[kMaxRows];                 // routing weights of the current task's pairs (DOWN)
 };
 static_assert(sizeof(Misc) <= kMiscBytes, "misc region too small");
 
@@ -314,6 +327,27 @@ __device__ __forceinline__ const float* layer_in(const KParams& p, int l) {
 __device__ __forceinline__ const float* layer_h1(const KParams& p, int l) {
   return p.attn ? act_f(p, l, p.al.h1) : layer_in(p, l);
 }
+// The same for any row group g of the launch (tasks of a row-group launch
+// read and write the rows of every group).
+__device__ __forceinline__ char* grp_act(const KParams& p, int g, int l) {
+  return p.act + (size_t)g * p.act_gstride + (size_t)l * p.al.stride;
+}
+__device__ __forceinline__ const float* grp_h1(const KParams& p, int g, int l) {
+  if (p.attn) return reinterpret_cast<const float*>(grp_act(p, g, l) + p.al.h1);
+  if (l == 0) return p.hidden_in + (size_t)g * p.M * p.d;
+  return reinterpret_cast<const float*>(grp_act(p, g, l - 1) + p.al.h2);
+}
+// every group's routing of layer l (in group 0's workspace)
+__device__ __forceinline__ int* rtab_ids(const KParams& p, int l) {
+  return reinterpret_cast<int*>(grp_act(p, 0, l) + p.al.rtab);
+}
+__device__ __forceinline__ float* rtab_wts(const KParams& p, int l) {
+  return reinterpret_cast<float*>(rtab_ids(p, l) + (size_t)p.n_groups * p.M * p.k);
+}
+// a task entry's parts: expert, row of the launch, top-k slot
+__device__ __forceinline__ int ent_expert(unsigned en) { return (int)(en >> 9); }
+__device__ __forceinline__ int ent_row(unsigned en) { return (int)((en >> 3) & 63u); }
+__device__ __forceinline__ int ent_slot(unsigned en) { return (int)(en & 7u); }
 // q = a / b, r = a % b for 0 <= a < 2^24, 1 <= b and a / b < 2^22: the float
 // estimate of the quotient is within one of the truth, and one correction
 // each way makes it exact.  A few instructions instead of the generic
@@ -348,7 +382,7 @@ __device__ __forceinline__ void my_range(int n, const KParams& p, int& lo, int& 
 // of static phases can be built before the phase starts, which is what lets
 // the ring run ahead across phase boundaries.
 
-enum PlanKind { PK_NONE = 0, PK_QKV, PK_ATTN, PK_WO, PK_RS, PK_RG, PK_DOWN, PK_DOWNA };
+enum PlanKind { PK_NONE = 0, PK_QKV, PK_ATTN, PK_WO, PK_RS, PK_RG, PK_DOWN, PK_DOWNA, PK_RGT, PK_DOWNT };
 
 struct Plan {
   int kind;
@@ -421,6 +455,22 @@ __device__ __forceinline__ TileSrc plan_tile(const Plan& P, int i, const Misc* m
       const QR uj = divmod_small(P.lo + i, P.nj);
       const int u = uj.q, jb = uj.r;
       return TileSrc{P.b0 + (((size_t)ms->uni[u] * P.d + (size_t)jb * P.rpt) << P.lrb), kTileBytes};
+    }
+    case PK_RGT: {  // shared down as PK_RG, then (task, f-block) pairs
+      if (i < P.n1) {
+        const QR su = divmod_small(i, P.nj);
+        const int s = su.q, unit = P.lo + su.r;
+        return TileSrc{P.b0 + (((size_t)s * P.d + (size_t)unit * P.rpt) << P.lrb), kTileBytes};
+      }
+      const int k = i - P.n1;
+      const QR tf = divmod_small(P.lo2 + (k >> 1), P.fb_per);
+      const int e = ent_expert(ms->tent[ms->tbeg[tf.q]]), fb = tf.r;
+      return TileSrc{((k & 1) ? P.b2 : P.b1) + (((size_t)e * P.F + (size_t)fb * P.rpt2) << P.lrb2), kTileBytes};
+    }
+    case PK_DOWNT: {  // flat (task, j-block) index, task-major
+      const QR tj = divmod_small(P.lo + i, P.nj);
+      const int e = ent_expert(ms->tent[ms->tbeg[tj.q]]), jb = tj.r;
+      return TileSrc{P.b0 + (((size_t)e * P.d + (size_t)jb * P.rpt) << P.lrb), kTileBytes};
     }
     default:
       return TileSrc{nullptr, 0};
@@ -613,6 +663,39 @@ __device__ __forceinline__ Plan plan_down_a(const KParams& p, const Misc* ms, in
   P.lo2 = lo;
   P.n1 = hi - lo;
   P.b0 = (const char*)layer_tab(p)[l].w_down;
+  return P;
+}
+
+// Row-group launches: the routed tiles of the launch's tasks, split over all
+// of its workgroups (c * n stays below 2^32).
+__device__ __forceinline__ void grid_range(int n, const KParams& p, int& lo, int& hi) {
+  const unsigned c = blockIdx.x, ncu = (unsigned)p.n_cu;
+  lo = (int)((c * (unsigned)n) / ncu);
+  hi = (int)(((c + 1) * (unsigned)n) / ncu);
+}
+// RG: this group's shared-down tiles (as plan_rg), then this workgroup's
+// range of the (task, f-block) gate/up pairs
+template <typename WT>
+__device__ __forceinline__ Plan plan_rg_t(const KParams& p, const Misc* ms, int l) {
+  Plan P = plan_rg<WT>(p, ms, l, false);
+  P.kind = PK_RGT;
+  int l2, h2;
+  grid_range(ms->n_task * P.fb_per, p, l2, h2);
+  P.lo2 = l2;
+  P.n = P.n1 + 2 * (h2 - l2);
+  return P;
+}
+// DOWN, first half: this workgroup's range of the (task, j-block) tiles;
+// lo2 / n1 are this group's output column blocks for the second half
+template <typename WT>
+__device__ __forceinline__ Plan plan_down_t(const KParams& p, const Misc* ms, int l) {
+  Plan P = plan_down_a<WT>(p, ms, l);
+  P.kind = PK_DOWNT;
+  P.U = ms->n_task;
+  int lo, hi;
+  grid_range(P.U * P.nj, p, lo, hi);
+  P.lo = lo;
+  P.n = hi - lo;
   return P;
 }
 
@@ -862,18 +945,23 @@ __device__ __forceinline__ void load_x<uint16_t, 8>(XRegs<uint16_t, 8>& xr, cons
     }
   }
 }
-template <>
-__device__ __forceinline__ void load_x_norm<uint16_t, 8>(XRegs<uint16_t, 8>& xr, Smem sm, const float* src, int ld,
-                                                         const uint16_t* gam, int M, int d, float eps, int wave,
-                                                         int lane, int lrb) {
+// The 8-row loader for rows given by row(t) (a pointer to the row's first
+// element, called with t < n only; rows t >= n are zero).  set_rinv(t, v)
+// receives 1/rms of row t < n after a workgroup synchronisation inside.
+// lead: synchronise first, for a caller that may still be reading the
+// sum-of-squares slots of an earlier call.
+template <class RowFn, class RinvFn>
+__device__ __forceinline__ void load_x_norm8(XRegs<uint16_t, 8>& xr, Smem sm, RowFn row, int n, const uint16_t* gam,
+                                             int d, float eps, int wave, int lane, int lrb, RinvFn set_rinv,
+                                             bool lead) {
   const int t4 = lane & 3, b = lane >> 2;
   const int k0 = m8_kq(wave, lrb) + b * 4;
   float ss[2] = {0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = t4 + 4 * h;
-    const bool ok = t < M;
-    const float* s = src + (size_t)(ok ? t : 0) * ld + k0;
+    const bool ok = t < n;
+    const float* s = row(ok ? t : 0) + k0;
 #pragma unroll
     for (int kc = 0; kc < 16; ++kc) {
       float4 a = *reinterpret_cast<const float4*>(s + kc * 64);
@@ -894,18 +982,42 @@ __device__ __forceinline__ void load_x_norm<uint16_t, 8>(XRegs<uint16_t, 8>& xr,
     x += dpp<kDppRor8>(x);
     ss[h] = sum_rows(x);
   }
+  if (lead) __syncthreads();
   if (b == 0) {
     sm.misc->ssq[wave * kMaxRows + t4] = ss[0];
     sm.misc->ssq[wave * kMaxRows + t4 + 4] = ss[1];
   }
   __syncthreads();
-  if ((int)threadIdx.x < M) {
+  if ((int)threadIdx.x < n) {
     const int t = threadIdx.x;
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) tot += sm.misc->ssq[w * kMaxRows + t];
     const float rpt = (float)(kTileBytes >> lrb);
-    sm.misc->rinv[t] = 1.0f / sqrtf(tot / (rpt * (float)d) + eps);
+    set_rinv(t, 1.0f / sqrtf(tot / (rpt * (float)d) + eps));
+  }
+}
+template <>
+__device__ __forceinline__ void load_x_norm<uint16_t, 8>(XRegs<uint16_t, 8>& xr, Smem sm, const float* src, int ld,
+                                                         const uint16_t* gam, int M, int d, float eps, int wave,
+                                                         int lane, int lrb) {
+  load_x_norm8(
+      xr, sm, [&](int t) { return src + (size_t)t * ld; }, M, gam, d, eps, wave, lane, lrb,
+      [&](int t, float v) { sm.misc->rinv[t] = v; }, false);
+}
+// 8 rows of plain x from rows given by row(t) (called with t < n only; rows
+// t >= n repeat row 0, which the token mask then drops)
+template <class RowFn>
+__device__ __forceinline__ void load_x8_rows(XRegs<uint16_t, 8>& xr, RowFn row, int n, int wave, int lane, int lrb) {
+  const int t4 = lane & 3, b = lane >> 2;
+  const int k0 = m8_kq(wave, lrb) + b * 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = t4 + 4 * h;
+    const float* s = row(t < n ? t : 0) + k0;
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc)
+      split_bf16x4(*reinterpret_cast<const float4*>(s + kc * 64), xr.hi[h][kc], xr.lo[h][kc]);
   }
 }
 
@@ -1026,7 +1138,11 @@ __device__ __forceinline__ void gemv_group<uint16_t, 8>(Smem sm, const Stream& s
   // bit 5 (tokens t < 4 stay where the bit is clear), bit 4, then bit 2 by a
   // row rotation by 4 (the lanes it pairs always differ in bit 2) and a plain
   // sum over bit 3 by a rotation by 8.  Lane l with bit 3 clear then holds
-  // token t = 4*bit5 + 2*bit4 + bit2 of row r.
+  // token t = 4*bit5 + 2*bit4 + bit2 of row r.  Lanes with bit 2 clear take
+  // the rotation one way, lanes with it set the other way, so that the
+  // tokens of both kinds add the same pairs of lanes in the same tree (only
+  // the operand order of an addition differs, which is exact): a token's
+  // sum does not depend on its place among the 8 rows.
   float w4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) w4[i] = swap32_sum(d0[i], d1[i]);
@@ -1034,7 +1150,8 @@ __device__ __forceinline__ void gemv_group<uint16_t, 8>(Smem sm, const Stream& s
 #pragma unroll
   for (int i = 0; i < 2; ++i) w2[i] = swap16_sum(w4[i], w4[2 + i]);
   const bool b2 = (lane >> 2) & 1;
-  float x = (b2 ? w2[1] : w2[0]) + dpp<kDppRor4>(b2 ? w2[0] : w2[1]);
+  const float from_dn = dpp<kDppRor4>(w2[0]), from_up = dpp<kDppRor12>(w2[1]);
+  float x = b2 ? w2[1] + from_up : w2[0] + from_dn;
   x += dpp<kDppRor8>(x);
   if (((lane >> 3) & 1) == 0 && r < g) {
     const bool b4 = (lane >> 4) & 1, b5 = (lane >> 5) & 1;
@@ -1991,6 +2108,94 @@ __device__ __forceinline__ void phase_rg(const KParams& p, Smem sm, int l, Strea
       });
 }
 
+// RG of a row-group launch (8-row token groups, bf16 weights): this group's
+// shared-down tiles as in phase_rg, then this workgroup's range of the
+// tasks' gate/up pairs.  A task's x rows are its rows' h1, normed with the
+// same arithmetic as the groups' own RS (the register layout does not
+// depend on a row's place in the group), loaded when the task starts; each
+// row's 1/rms goes to rinv_row.  Outputs go to the rows' own groups.
+template <typename WT>
+__device__ __forceinline__ void phase_rg_t(const KParams& p, Smem sm, int l, Stream& st, const Plan& P,
+                                           const Plan& N, int early) {
+  constexpr int MT = 8;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int d = p.d, F = p.F, k = p.k, M = p.M, S = p.S;
+  float* ys = act_w(p, l, p.al.y_s);
+  zero_part(sm);
+  if (early > 0) wait_tiles_ahead(early);
+  else wait_all();
+  __syncthreads();
+  Misc* ms = sm.misc;
+  constexpr int kRound = (kPartAcc / (kWaves * Slots<WT>::C * MT)) & ~1;  // even: a gate/up pair stays in one round
+  const int n1 = P.n1, n = P.n, nj = P.nj, lrb = P.lrb, lrb2 = P.lrb2, rpt = P.rpt, rpt2 = P.rpt2;
+  const int fb_per = P.fb_per, sd_lo = P.lo, p_lo = P.lo2;
+  const WT* gam = reinterpret_cast<const WT*>(layer_tab(p)[l].moe_norm);
+  XRegs<WT, MT> xw;  // a_s rows for the shared-down tiles, then a task's rows
+  int xt = -1;       // task whose rows the registers hold
+  run_gemv<WT, MT, PK_RGT, PK_DOWNT, false>(
+      sm, st, P, N, xw,
+      [&](int i, Seg<MT>& sg) {
+        seg_all<MT>(sg, M);
+        if (i < n1) {  // expert s of the shared down projection, all of this CU's j-blocks
+          const int sx = i / nj;
+          load_x_rows<WT, MT>(xw, sm.xs, [&](int t) { return (t * S + sx) * F; }, wave, lane, lrb);
+          sg.end = i + nj;
+          sg.blk0 = 0;
+          sg.accum = true;
+          sg.round_end = sg.end == n1;
+        } else {
+          const int k0 = i - n1;
+          const int tk = (p_lo + k0 / 2) / fb_per;
+          const int e0 = ms->tbeg[tk], cnt = ms->tbeg[tk + 1] - e0;
+          int end = n1 + min(n - n1, (k0 / kRound + 1) * kRound);
+          end = min(end, n1 + 2 * ((tk + 1) * fb_per - p_lo));  // one run per task
+          sg.tmask = (1u << cnt) - 1u;
+          if (tk != xt) {
+            xt = tk;
+            load_x_norm8(
+                xw, sm,
+                [&](int t) {
+                  const int r = ent_row(ms->tent[e0 + t]);
+                  return grp_h1(p, r / M, l) + (size_t)(r % M) * d;
+                },
+                cnt, gam, d, p.eps, wave, lane, lrb2,
+                [&](int t, float v) { ms->rinv_row[ent_row(ms->tent[e0 + t])] = v; }, true);
+          }
+          sg.end = end;
+          sg.blk0 = k0 % kRound;
+          sg.accum = false;
+          sg.round_end = end == n || ((end - n1) % kRound) == 0;
+        }
+      },
+      [&](int first, int last) {
+        if (first < n1) {
+          // shared-down j-blocks of this CU: y_s[t][j]
+          for (int it = threadIdx.x; it < nj * rpt * M; it += kThreads) {
+            const int u = it / (rpt * M), q = (it / M) % rpt, t = it % M;
+            const int j = (sd_lo + u) * rpt + q;
+            st_dev(ys + (size_t)t * d + j, part_row<WT, MT>(sm.part, u, q, lrb, t));
+          }
+        } else {
+          const int k0 = first - n1;
+          const int npairs_r = (last - first + 1) / 2;
+          for (int it = threadIdx.x; it < npairs_r * rpt2 * MT; it += kThreads) {
+            const int pr = it / (rpt2 * MT), q = (it / MT) % rpt2, t = it % MT;
+            const int pj = p_lo + k0 / 2 + pr;
+            const QR tf = divmod_small(pj, fb_per);
+            const int e0 = ms->tbeg[tf.q];
+            if (t >= ms->tbeg[tf.q + 1] - e0) continue;
+            const unsigned en = ms->tent[e0 + t];
+            const int r = ent_row(en), f = tf.r * rpt2 + q;
+            const float ri = ms->rinv_row[r];
+            const float gv = part_row<WT, MT>(sm.part, 2 * pr, q, lrb2, t) * ri;
+            const float uv = part_row<WT, MT>(sm.part, 2 * pr + 1, q, lrb2, t) * ri;
+            float* a = reinterpret_cast<float*>(grp_act(p, r / M, l) + p.al.a);
+            st_dev(a + ((size_t)(r % M) * k + ent_slot(en)) * F + f, gv / (1.f + __expf(-gv)) * uv);
+          }
+        }
+      });
+}
+
 // DOWN: for this CU's j-blocks (output columns), accumulate the union
 // experts one after another (expert-major, so an expert's x rows are loaded
 // once), each row weighted by its routing weight; then h2 = h1 + y_s + sum.
@@ -2167,6 +2372,80 @@ __device__ __forceinline__ void phase_down_a(const KParams& p, Smem sm, int l, S
       });
 }
 
+// DOWN of a row-group launch, first half: this workgroup's range of the
+// (task, j-block) tiles; a task's x rows are a[row][slot] of its pairs, in
+// the rows' own groups, weighted by their routing weights; the products go
+// to yp[row][slot][j] of the rows' groups.  The residual h1 + y_s of this
+// group's second-half columns goes to LDS here.
+template <typename WT>
+__device__ __forceinline__ void phase_down_a_t(const KParams& p, Smem sm, int l, Stream& st, const Plan& P,
+                                               const Plan& N) {
+  constexpr int MT = 8;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int d = p.d, F = p.F, k = p.k, M = p.M;
+  const int nj = P.nj, rpt = P.rpt, lrb = P.lrb, lo = P.lo, n = P.n;
+  const float* h1 = layer_h1(p, l);
+  const float* ys = act_f(p, l, p.al.y_s);
+  const float* wts = rtab_wts(p, l);
+  zero_part(sm);
+  load_res(sm, h1, p.S > 0 ? ys : nullptr, d, P.lo2 * rpt, P.n1 * rpt, M);
+  wait_all();
+  __syncthreads();
+  Misc* ms = sm.misc;
+  constexpr int kRound = kPartAcc / (kWaves * Slots<WT>::C * MT);
+  const int lrpt = 13 - lrb;  // log2 rows per tile
+  XRegs<WT, MT> xr;
+  int xt = -1;  // task whose x rows the registers hold
+  run_gemv<WT, MT, PK_DOWNT, kAnyKind>(
+      sm, st, P, N, xr,
+      [&](int i, Seg<MT>& sg) {
+        const int tk = (lo + i) / nj;
+        const int e0 = ms->tbeg[tk], cnt = ms->tbeg[tk + 1] - e0;
+        sg.end = min(min(n, (tk + 1) * nj - lo), (i / kRound + 1) * kRound);
+        sg.blk0 = i % kRound;
+        sg.accum = false;
+        sg.round_end = sg.end == n || sg.end % kRound == 0;
+        sg.tmask = (1u << cnt) - 1u;
+        if (tk != xt) {
+          xt = tk;
+          // every wave has taken the last task's weights before they change
+          __syncthreads();
+          if ((int)threadIdx.x < MT) {
+            const int t = threadIdx.x;
+            const unsigned en = ms->tent[e0 + min(t, cnt - 1)];
+            ms->task_w[t] = t < cnt ? wts[ent_row(en) * k + ent_slot(en)] : 0.f;
+          }
+          load_x8_rows(
+              xr,
+              [&](int t) {
+                const unsigned en = ms->tent[e0 + t];
+                const int r = ent_row(en);
+                return reinterpret_cast<const float*>(grp_act(p, r / M, l) + p.al.a) +
+                       ((size_t)(r % M) * k + ent_slot(en)) * F;
+              },
+              cnt, wave, lane, lrb);
+          __syncthreads();
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) sg.tw[t] = ms->task_w[t];
+      },
+      [&](int first, int last) {
+        for (int it = threadIdx.x; it < (last - first + 1) << lrpt; it += kThreads) {
+          const int b = it >> lrpt, r = it & (rpt - 1);
+          const int g = lo + first + b;
+          const QR tj = divmod_small(g, nj);
+          const int e0 = ms->tbeg[tj.q], cnt = ms->tbeg[tj.q + 1] - e0;
+          for (int t = 0; t < cnt; ++t) {
+            const unsigned en = ms->tent[e0 + t];
+            const int row = ent_row(en);
+            float* yp = reinterpret_cast<float*>(grp_act(p, row / M, l) + p.al.yp);
+            st_dev(yp + ((size_t)(row % M) * k + ent_slot(en)) * d + (size_t)tj.r * rpt + r,
+                   part_row<WT, MT>(sm.part, b, r, lrb, t));
+          }
+        }
+      });
+}
+
 // DOWN with several rows, second half: h2[t][j] = h1 + y_s + the sum of
 // yp[t][slot][j] over the row's top-k slots, for this CU's output columns
 // [c0, c0 + ncol) (the residual is in LDS from the first half).
@@ -2248,47 +2527,91 @@ __device__ __forceinline__ bool launch_setup(const KParams& p, Smem sm) {
   return true;
 }
 
-// Row groups: the expert union of all groups of the launch.  Each group's
-// routing (route_rank, the same in all its workgroups) gives its own union;
-// one workgroup per group publishes it as a mask (write-once per launch),
-// and after the next grid barrier every workgroup replaces its union by the
-// union of all masks, in ascending expert order.  All groups then walk the
-// same routed tiles in the same order (a group's rows not routed to an
-// expert contribute nothing), so position c of every group loads the same
-// tile at about the same time and the copies meet in the XCD's L2.
-__device__ __forceinline__ void publish_union(const KParams& p, Smem sm, int l) {
+// Row groups: the routed work of all groups of the launch as tasks.  Each
+// group's routing (route_rank, the same in all its workgroups) is published
+// by one workgroup per group (write-once per launch); after the next grid
+// barrier every workgroup builds the same task table from all of it
+// (build_tasks), and the routed tiles of the tasks are spread over every
+// workgroup of the launch.  An expert chosen by n rows of the launch is then
+// streamed ceil(n / kMaxRows) times, instead of once per group.
+__device__ __forceinline__ void publish_routing(const KParams& p, Smem sm, int l) {
   if (vcu_of(p) != 0) return;
-  unsigned* um = reinterpret_cast<unsigned*>(p.act + (size_t)l * p.al.stride + p.al.umask) + 2 * grp_of(p);
+  const int mk_ = p.M * p.k, g = grp_of(p);
+  int* ids = rtab_ids(p, l) + g * mk_;
+  float* wts = rtab_wts(p, l) + g * mk_;
   const Misc* ms = sm.misc;
-  if (threadIdx.x < 64) {
-    const bool in = (int)threadIdx.x < ms->n_uni;
-    const int e = ms->uni[in ? threadIdx.x : 0];
-    unsigned long long m = 0;
-    // OR of the lanes' bits: one bit per union expert
-    const unsigned long long bit = in ? (1ull << e) : 0ull;
-    unsigned lo = (unsigned)bit, hi = (unsigned)(bit >> 32);
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      lo |= __shfl_xor(lo, sh);
-      hi |= __shfl_xor(hi, sh);
-    }
-    m = ((unsigned long long)hi << 32) | lo;
-    if (threadIdx.x == 0) {
-      st_dev_u(um, (unsigned)m);
-      st_dev_u(um + 1, (unsigned)(m >> 32));
-    }
+  for (int i = threadIdx.x; i < mk_; i += kThreads) {
+    st_dev_u(reinterpret_cast<unsigned*>(ids + i), (unsigned)ms->ids[i]);
+    st_dev(wts + i, ms->wts[i]);
   }
 }
-__device__ __forceinline__ void merge_unions(const KParams& p, Smem sm, int l) {
-  const unsigned* um = reinterpret_cast<const unsigned*>(p.act + (size_t)l * p.al.stride + p.al.umask);
+
+// The task table of layer l from the published routing: per expert in
+// ascending id order, its (row, slot) pairs with rows ascending, cut into
+// tasks of at most kMaxRows pairs.  Wave w counts and places the pairs of a
+// quarter of the rows, lane e those of expert e; the counts' prefix sums
+// over the experts give each expert's first entry and first task.  Scratch
+// in the part region, which is free until the RG GEMV starts.
+__device__ __forceinline__ void build_tasks(const KParams& p, Smem sm, int l) {
   Misc* ms = sm.misc;
-  if (threadIdx.x < 64) {
-    const int e = threadIdx.x;
-    bool in = false;
-    for (int g = 0; g < p.n_groups; ++g) in |= ((um[2 * g + (e >> 5)] >> (e & 31)) & 1u) != 0;
-    in &= e < p.E;
-    const unsigned long long mm = __ballot(in);
-    if (in) ms->uni[__popcll(mm & ((1ull << e) - 1ull))] = e;
-    if (e == 0) ms->n_uni = __popcll(mm);
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int nr = p.n_groups * p.M, k = p.k;
+  const int* ids = rtab_ids(p, l);
+  unsigned char* idb = reinterpret_cast<unsigned char*>(sm.part);  // [nr][8] expert ids, 0xff past k
+  int* cnt = reinterpret_cast<int*>(sm.part) + kMaxGroups * kMaxRows * 8 / 4;  // [kWaves][64]
+  static_assert(kMaxGroups * kMaxRows * 8 + kWaves * 64 * 4 <= kPartAcc * 4, "task scratch does not fit");
+  for (int it = threadIdx.x; it < nr * 8; it += kThreads) {
+    const int r = it >> 3, s = it & 7;
+    idb[it] = (unsigned char)(s < k ? ids[r * k + s] : 0xff);
+  }
+  __syncthreads();
+  const int r0 = wave * nr / kWaves, r1 = (wave + 1) * nr / kWaves;
+  const int e = lane;
+  int c = 0;
+  for (int r = r0; r < r1; ++r) {
+    const unsigned long long v = *reinterpret_cast<const unsigned long long*>(idb + r * 8);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) c += (int)((v >> (8 * s)) & 0xffu) == e ? 1 : 0;
+  }
+  cnt[wave * 64 + e] = c;
+  __syncthreads();
+  if (wave == 0) {
+    int n_e = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) n_e += cnt[w * 64 + e];
+    const int nt_e = (n_e + kMaxRows - 1) / kMaxRows;
+    // inclusive prefix sums over the lanes
+    int ie = n_e, it = nt_e;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int ue = __shfl_up(ie, sh), ut = __shfl_up(it, sh);
+      if (lane >= sh) {
+        ie += ue;
+        it += ut;
+      }
+    }
+    const int eb = ie - n_e, tb = it - nt_e;
+    for (int q = 0; q < nt_e; ++q) ms->tbeg[tb + q] = (unsigned short)(eb + q * kMaxRows);
+    if (lane == 63) {
+      ms->tbeg[it] = (unsigned short)ie;
+      ms->n_task = it;
+    }
+    // first entry of each wave's pairs of expert e
+    int off = eb;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int cw = cnt[w * 64 + e];
+      cnt[w * 64 + e] = off;
+      off += cw;
+    }
+  }
+  __syncthreads();
+  int pos = cnt[wave * 64 + e];
+  for (int r = r0; r < r1; ++r) {
+    const unsigned long long v = *reinterpret_cast<const unsigned long long*>(idb + r * 8);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if ((int)((v >> (8 * s)) & 0xffu) == e) ms->tent[pos++] = (unsigned short)((e << 9) | (r << 3) | s);
   }
   __syncthreads();
 }
@@ -2307,6 +2630,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
   long long* stamp = p.stamps ? p.stamps + (size_t)blockIdx.x * 4 * (p.barriers + 1) : nullptr;
   XRegs<WT, MT> xr_moe;
   Stream st{0, 0, stamp, Win{0u, 0u, kNoWin}, Win{0u, 0u, kNoWin}, 0, lds_addr(sm.ring), p.n_groups > 1};
+  // row groups in one launch: 8-row token groups with bf16 weights only (the
+  // host runs other row groups one launch each)
+  constexpr bool kTasks = MT == 8 && std::is_same<WT, uint16_t>::value;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   // phase i owns slots 4i..4i+3: start (after barrier i), tile loop start,
   // tile loop end, end (before barrier i+1)
@@ -2353,21 +2679,33 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
     {
       rg_stage(p, sm, l);
       route_rank(p, sm, l);
-      if (p.n_groups > 1) {  // all row groups stream the union of their experts
-        publish_union(p, sm, l);
+      if (kTasks && p.n_groups > 1) {  // the routed work of all row groups as tasks
+        if constexpr (kTasks) {
+          publish_routing(p, sm, l);
+          MK_SYNC();
+          build_tasks(p, sm, l);
+          cur = plan_rg_t<WT>(p, ms, l);  // same first tiles as the prefetched plan
+          const Plan nxt = plan_down_t<WT>(p, ms, l);
+          const int pre = st.issued;
+          st.fill<PK_RGT, PK_DOWNT>(sm, cur, nxt, 0, wave, lane);
+          route_tables(p, sm, l);  // the trace
+          phase_rg_t<WT>(p, sm, l, st, cur, nxt, st.issued - pre);
+          MK_SYNC();
+          st.advance(cur);
+          cur = nxt;
+        }
+      } else {
+        cur = plan_rg<WT>(p, ms, l, true);  // same first tiles as the prefetched plan
+        const Plan nxt = MT == 1 ? plan_down<WT>(p, ms, l) : plan_down_a<WT>(p, ms, l);
+        // the routed tiles start streaming as soon as the union is known
+        const int pre = st.issued;
+        st.fill<PK_RG, MT == 1 ? PK_DOWN : PK_DOWNA>(sm, cur, nxt, 0, wave, lane);
+        route_tables(p, sm, l);
+        phase_rg<WT, MT>(p, sm, l, st, cur, nxt, xr_moe, st.issued - pre);
         MK_SYNC();
-        merge_unions(p, sm, l);
+        st.advance(cur);
+        cur = nxt;
       }
-      cur = plan_rg<WT>(p, ms, l, true);  // same first tiles as the prefetched plan
-      const Plan nxt = MT == 1 ? plan_down<WT>(p, ms, l) : plan_down_a<WT>(p, ms, l);
-      // the routed tiles start streaming as soon as the union is known
-      const int pre = st.issued;
-      st.fill<PK_RG, MT == 1 ? PK_DOWN : PK_DOWNA>(sm, cur, nxt, 0, wave, lane);
-      route_tables(p, sm, l);
-      phase_rg<WT, MT>(p, sm, l, st, cur, nxt, xr_moe, st.issued - pre);
-      MK_SYNC();
-      st.advance(cur);
-      cur = nxt;
     }
     {
       const Plan nxt = (l + 1 < p.L) ? (p.attn ? plan_qkv<WT>(p, l + 1) : plan_rs<WT>(p, l + 1)) : none;
@@ -2378,7 +2716,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_step_kernel(KParams kp) {
         cur = nxt;
       } else {
         const int c0 = cur.lo2 * cur.rpt, ncol = cur.n1 * cur.rpt;
-        phase_down_a<WT, MT>(p, sm, l, st, cur, nxt);
+        if (kTasks && p.n_groups > 1) {
+          if constexpr (kTasks) phase_down_a_t<WT>(p, sm, l, st, cur, nxt);
+        } else {
+          phase_down_a<WT, MT>(p, sm, l, st, cur, nxt);
+        }
         MK_SYNC();
         st.advance(cur);
         cur = nxt;
@@ -2474,6 +2816,7 @@ static int mk_pick(const mk::KParams& p, bool phased, const void** fn, int* idx)
   if (p.M < 1 || p.M > kMaxRows) return -2;
   if (p.attn && p.n_seq * p.G * p.q_groups * p.n_splits > p.vncu) return -2;
   if (p.n_groups < 1 || p.n_groups * p.vncu != p.n_cu || (p.n_groups > 1 && p.vncu != 8 << p.cpx_log2)) return -2;
+  if (p.n_groups > 1 && (p.wide || p.M != kMaxRows || p.n_groups > kMaxGroups)) return -2;  // tasks: 8-row bf16 groups
   const int Q = p.attn ? p.q_per_task : 0;
   const bool one = p.M == 1;
   // instantiations: weight dtype x token group (1 or 8) x attention task

@@ -16,6 +16,7 @@ constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kDppRor4 = 0x124;  // row_ror:4
 constexpr int kDppRor8 = 0x128;  // row_ror:8
+constexpr int kDppRor12 = 0x12C; // row_ror:12 (a rotation by 4 the other way)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));

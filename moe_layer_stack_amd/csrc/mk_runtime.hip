@@ -217,14 +217,14 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   h->n_cu = prop.multiProcessorCount;
   const int M = launch_rows(c);
   const int n_seq = M / c.rows_per_seq;
-  // A step of more than kMaxRows rows runs its groups of kMaxRows rows in one
-  // launch when the CUs split into equal groups with the same power-of-two
-  // number on every XCD (workgroups are dealt to the 8 XCDs round-robin);
-  // otherwise as one launch per group.
+  // A step of more than kMaxRows rows with bf16 weights runs its groups of
+  // kMaxRows rows in one launch when the CUs split into equal groups with the
+  // same power-of-two number on every XCD (workgroups are dealt to the 8 XCDs
+  // round-robin); otherwise as one launch per group.
   h->n_groups = 1;
   h->vncu = h->n_cu;
   h->cpx_log2 = 0;
-  if (c.rows > M) {
+  if (c.rows > M && c.dtype == MK_BF16) {
     const int ng = c.rows / M;
     const int per = h->n_cu / ng;
     if (h->n_cu % (8 * ng) == 0 && ((per / 8) & (per / 8 - 1)) == 0) {
@@ -293,7 +293,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   // several rows: the routed down projection runs in two phases (expert-major
   // products, then the per-column sum), one more barrier per layer
   // and row groups in one launch meet at one more barrier per layer, where
-  // they exchange their expert unions
+  // they publish their routing
   h->barriers = c.n_layers * ((c.has_attn ? 6 : 3) + (M > 1 ? 1 : 0) + (h->n_groups > 1 ? 1 : 0)) - 1;
   // LDS: fixed carve-up (ring, x staging, per-row partial sums, misc)
   h->x_bytes = mk::kXsBytes;
@@ -318,7 +318,7 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   al.y_s = take((size_t)M * d * 4);
   al.yp = take(M > 1 ? (size_t)M * k * d * 4 : 0);
   al.h2 = take((size_t)M * d * 4);
-  al.umask = take((size_t)h->n_groups * 8);
+  al.rtab = take(h->n_groups > 1 ? (size_t)h->n_groups * M * c.top_k * 8 : 0);
   al.stride = align256(off);
   h->al = al;
   h->act_bytes = al.stride * c.n_layers * h->n_groups;  // a workspace per row group
@@ -389,6 +389,7 @@ int mk_get_info(const mk_handle* h, mk_info* info) {
   info->lds_bytes = h->ring_tiles * mk::kSlotBytes + h->x_bytes + mk::kPartBytes + mk::kMiscBytes;
   info->barriers_per_step = h->barriers;
   info->attn_splits = h->n_splits;
+  info->launches_per_step = h->n_groups > 1 ? 1 : h->cfg.rows / launch_rows(h->cfg);
   info->workspace_bytes =
       (int64_t)(h->act_bytes + SyncLayout::kWords * 4 + sizeof(DevLayer) * h->cfg.n_layers);
   return MK_OK;
@@ -455,7 +456,7 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
     p.act_gstride = grouped ? h->al.stride * c.n_layers : 0;
     p.ring_tiles = h->ring_tiles;
     p.x_bytes = h->x_bytes;
-    // barriers of this launch (the row groups' union exchange only when grouped)
+    // barriers of this launch (the row groups' routing exchange only when grouped)
     p.barriers = grouped || h->n_groups == 1 ? h->barriers
                                              : c.n_layers * ((c.has_attn ? 6 : 3) + (Mg > 1 ? 1 : 0)) - 1;
     p.timeout_ticks = h->watchdog_ticks;

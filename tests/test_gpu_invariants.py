@@ -131,6 +131,33 @@ def test_repeated_steps_are_bitwise_identical(env, name):
         run.close()
 
 
+def test_row_order_does_not_change_a_row(env):
+    """A row's arithmetic does not depend on its place among the 8 rows of a
+    step: reversing the rows (every row changes all three bits of its index)
+    reverses the outputs and the routing trace bit for bit.  The one-launch
+    64-row verify relies on this: its routed work puts a row at any place of
+    an 8-row task."""
+    from parity_util import GpuRun
+    from synth.workloads import MOE16_B8
+    torch = env
+    w = MOE16_B8
+    _say(f"row order {w.name} L=2")
+    st = _stack(w, 2)
+    run = GpuRun(st)
+    try:
+        hid = st.hidden(0)
+        rev = torch.arange(w.M - 1, -1, -1, device="cuda")
+        a = run.step(hid, w.positions(0)).clone()
+        ta = [x.copy() for x in run.trace()]
+        b = run.step(hid[rev].contiguous(), w.positions(0)[::-1]).clone()
+        tb = run.trace()
+        assert torch.equal(a, b[rev]), (a - b[rev]).abs().max().item()
+        for x, y in zip(ta, tb):
+            assert np.array_equal(x, y[:, ::-1]), "trace differs under the row reversal"
+    finally:
+        run.close()
+
+
 def test_bad_positions_are_reported_and_the_handle_recovers(env):
     """A position outside [0, capacity) or two rows of one sequence at the same
     position: the step writes nothing it should not and the next mk_sync

@@ -40,6 +40,8 @@ def test_phased_equals_persistent(env, name, layers):
     st = DeviceStack(w, n_layers=layers)
     h = mk.mk_create(st.config(), st.layer_weights())
     try:
+        # every row of a step in one launch, row groups included (bf16 stacks)
+        assert mk.mk_get_info(h).launches_per_step == 1
         hid = st.hidden(0)
         pos = torch.tensor(w.positions(0), dtype=torch.int32, device="cuda")
         outs, traces = [], []
