@@ -334,16 +334,19 @@ def _pmc_rows(d, counter):
     return rows
 
 
-def parse_pmc(fetch_dir, write_dir, copy_mib):
-    """Per-launch HBM bytes of the batch-1 decode kernel from FETCH_SIZE and
+def parse_pmc(fetch_dir, write_dir, copy_mib, kernel="1, 1>", out_file=TRAFFIC_FILE):
+    """Per-launch HBM bytes of a decode kernel (the instantiation whose name
+    contains `kernel`; by default the batch-1 kernel) from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by the counter's reading for
-    the calibration copy of copy_mib MiB (read once, written once)."""
+    the calibration copy of copy_mib MiB (read once, written once).  Every
+    dispatch of that kernel in the runs counts (warm-up included), so each
+    pass should run one leg (--only)."""
     import numpy as np
-    out = {"source_hash": source_hash(), "copy_mib": copy_mib}
+    out = {"source_hash": source_hash(), "copy_mib": copy_mib, "kernel": kernel}
     for name, d in (("fetch", fetch_dir), ("write", write_dir)):
         counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
         rows = _pmc_rows(d, counter)
-        kern = [v for k, v in rows if "decode_step_kernel" in k and "1, 1>" in k]
+        kern = [v for k, v in rows if "decode_step_kernel" in k and kernel in k]
         copies = [v for k, v in rows if "copy" in k.lower()]
         if not kern or not copies:
             raise SystemExit(f"{counter}: no decode-kernel or copy dispatches under {d}")
@@ -355,10 +358,55 @@ def parse_pmc(fetch_dir, write_dir, copy_mib):
         out[f"{name}_bytes_per_launch"] = float(np.mean(kern)) * 1024.0 * scale
         out[f"{name}_launches"] = len(kern)
     out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
-        json.dump(out, fh, indent=1)
+    if out_file:
+        os.makedirs(os.path.dirname(os.path.abspath(out_file)), exist_ok=True)
+        with open(out_file, "w") as fh:
+            json.dump(out, fh, indent=1)
     print(json.dumps(out))
+
+
+def calib_copy(torch, mib):
+    """One device-to-device copy of mib MiB (read once, written once): the
+    reference dispatch that scales the HBM byte counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {mib} MiB")
+    del src, dst
+
+
+def only_leg(torch, mk, args):
+    """One leg by itself (its warm-up and timed steps), then the calibration
+    copy: the program of a counter pass, in which every dispatch of the leg's
+    kernel instantiation belongs to that leg."""
+    from synth.stack import DeviceStack
+    from synth.workloads import ATTN92_B8, MOE16_B8
+    leg = args.only
+    if leg.startswith("moe16"):
+        M = 1 if leg == "moe16_b1" else 8
+        st = DeviceStack(MOE16_B8, n_layers=args.layers)
+        w = MOE16_B8.with_(name=leg, M=M)
+        r = run_leg(torch, mk, st, w, M, 1, args.steps, args.warmup, trace_union=M > 1)
+    else:
+        M, rps = {"batch1": (1, 1), "batch8": (8, 1), "verify8": (8, 8), "verify64": (64, 8)}[leg]
+        w8 = ATTN92_B8.with_(cap_extra=max(64, 8 * (args.warmup + args.steps + 2)))
+        st = DeviceStack(w8, n_layers=args.layers)
+        w = w8.with_(M=M, rows_per_seq=rps)
+        r = run_leg(torch, mk, st, w, M, rps, args.steps, args.warmup, trace_union=M > 1)
+    log(f"{leg}: {r['ms_per_step']:.3f} ms/step, {r['achieved_gbps']:.0f} GB/s algorithmic "
+        f"({100 * r['frac']:.1f}% of peak), {r['launches']} launch(es) per step")
+    if args.calib_copy_mib:
+        calib_copy(torch, args.calib_copy_mib)
+    r.pop("union_per_layer", None)
+    print(json.dumps({"leg": leg, "layers": st.L, "source_hash": source_hash(),
+                      **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}}), flush=True)
+    torch.cuda.synchronize()
+    del st
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 def main():
@@ -381,11 +429,18 @@ def main():
     ap.add_argument("--maps-out", default=None,
                     help="after the teardown, copy /proc/self/maps to this file (to name the owner of an address "
                          "in a crash report at exit)")
+    ap.add_argument("--only", choices=["batch1", "batch8", "verify8", "verify64", "moe16_b1", "moe16_b8"],
+                    default=None, help="run only this leg (and --calib-copy-mib), print its record as JSON: the "
+                                       "program of a counter pass")
+    ap.add_argument("--pmc-kernel", default="1, 1>",
+                    help="with --parse-pmc: the decode-kernel instantiation to count (a substring of its name)")
+    ap.add_argument("--pmc-out", default=TRAFFIC_FILE, help="with --parse-pmc: the record's file ('' for none)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic record from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
     if args.parse_pmc:
-        parse_pmc(args.parse_pmc[0], args.parse_pmc[1], args.calib_copy_mib or 1024)
+        parse_pmc(args.parse_pmc[0], args.parse_pmc[1], args.calib_copy_mib or 1024, args.pmc_kernel,
+                  args.pmc_out)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode kernel runs on a single MI355X and this build has no "
@@ -404,6 +459,9 @@ def main():
     from synth.workloads import ATTN92_B8
     if not os.path.exists(synth.LIB):
         synth.build()
+    if args.only:
+        only_leg(torch, mk, args)
+        return
     need = args.warmup + args.steps
     n_seq = 1 if args.no_batch8 else 8
     w8 = ATTN92_B8.with_(cap_extra=max(64, 8 * (need + 2)), M=n_seq)  # room for 8 positions per spec step
@@ -503,14 +561,7 @@ def main():
                 log(f"cpu oracle, one thread: {one['value']:.4f} tok/s ({time.perf_counter() - t0:.1f} s)")
         optional("cpu_baseline", cpu_leg)
     if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {args.calib_copy_mib} MiB")
-        del src, dst
+        calib_copy(torch, args.calib_copy_mib)
     traffic = None
     tf = TRAFFIC_FILE
     if os.path.exists(tf):

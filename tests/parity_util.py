@@ -125,11 +125,11 @@ def oracle_walk(stack: DeviceStack, hidden_in, positions, gpu_ids, rows_per_seq=
     return h.astype(np.float32), rep
 
 
-def gpu_kv_rows(stack: DeviceStack, l, positions, rows_per_seq=1):
+def gpu_kv_rows(stack: DeviceStack, l, positions, rows_per_seq=1, seq0=0):
     """The GPU cache rows of layer l at the step's positions: (k, v) uint16
-    [M][G][hd], row r at sequence r // rows_per_seq."""
+    [M][G][hd], row r at sequence seq0 + r // rows_per_seq."""
     import torch
-    s = torch.as_tensor([r // rows_per_seq for r in range(len(positions))], device=stack.kc.device)
+    s = torch.as_tensor([seq0 + r // rows_per_seq for r in range(len(positions))], device=stack.kc.device)
     p = torch.as_tensor(np.asarray(positions, dtype=np.int64), device=stack.kc.device)
     k = stack.kc[l][s, :, p]  # [M][G][hd]
     v = stack.vc[l][s, :, p]
@@ -167,13 +167,14 @@ def kv_row_excess(gpu_bits, oracle_bits, extra=0.0):
     return float(np.max(diff / allowed)), int(np.count_nonzero(diff))
 
 
-def assert_kv_rows(stack: DeviceStack, rep, positions, rows_per_seq=1, layers=None, what="", tol=TOL_BF16):
+def assert_kv_rows(stack: DeviceStack, rep, positions, rows_per_seq=1, layers=None, what="", tol=TOL_BF16, seq0=0):
     """Every cache row the step wrote (every layer, row and kv head) against
     the oracle's bf16 row: within one bf16 step at the first layer, within one
-    step plus tol's max|d| (and tol's rel_l2 over the layer's rows) after it."""
+    step plus tol's max|d| (and tol's rel_l2 over the layer's rows) after it.
+    The rows are those of sequences seq0, seq0 + 1, ... of the cache."""
     worst0, worst, ndiff, n = 0.0, 0.0, 0, 0
     for l in (range(stack.L) if layers is None else layers):
-        gk, gv = gpu_kv_rows(stack, l, positions, rows_per_seq)
+        gk, gv = gpu_kv_rows(stack, l, positions, rows_per_seq, seq0)
         ok_, ov_ = rep["kv_rows"][l]
         for name, g, o in (("K", gk, ok_), ("V", gv, ov_)):
             assert g.shape == o.shape, (g.shape, o.shape)

@@ -387,13 +387,16 @@ def test_moe16_feedback_steps(env):
 
 
 @pytest.mark.timeout(1500)
-def test_attn92_full_depth_batch1_batch8_and_verify8(env):
+def test_attn92_full_depth_batch1_batch8_verify8_and_verify64(env):
     """The benchmark's stack at full depth (92 layers), every step against the
     oracle walked over the same bytes: batch 1 (sequence 0), batch 8 (all 8
-    rows, each its own sequence), and a verify pass of 8 rows of sequence 0.
-    Every step's output, expert sets, routing weights and all the K/V rows it
-    appended (92 layers x rows x 8 kv heads) are checked; batch-8 row 0 also
-    equals the batch-1 step."""
+    rows, each its own sequence), a verify pass of 8 rows of sequence 0, and
+    a verify pass of 8 rows of each of the 8 sequences in one launch, whose
+    sequence 5 is walked (its routed work ran in tasks mixed with the other
+    sequences' rows).  Every checked step's output, expert sets, routing
+    weights and all the K/V rows it appended (92 layers x rows x 8 kv heads)
+    are checked; batch-8 row 0 also equals the batch-1 step."""
+    import moe_layer_stack_amd as mk
     from parity_util import (GpuRun, assert_close, assert_kv_rows, assert_routing_weights, oracle_walk,
                              tolerances)
     from synth.workloads import ATTN92_B8
@@ -409,13 +412,16 @@ def test_attn92_full_depth_batch1_batch8_and_verify8(env):
                 _say(f"full depth {tag}: oracle at layer {l}")
         return oracle_walk(st, hid, pos, ids, rows_per_seq=rps, kv_hosts=kv_hosts, progress=progress)
 
-    def check(tag, out, hid, pos, run, rps, kv_hosts):
+    def check(tag, out, hid, pos, run, rps, kv_hosts, rows=None, seq0=0):
         ids, wts, logits = run.trace()
+        if rows is not None:  # a slice of the step's rows (whole sequences)
+            ids, wts, logits = ids[:, rows], wts[:, rows], logits[:, rows]
+        M = ids.shape[1]
         ref, rep = walk(tag, hid, pos, ids, rps, kv_hosts)
         assert not rep["mismatch"], (tag, rep["mismatch"][:3])
         c = assert_close(out.cpu().numpy(), ref, tol, f"full depth {tag}")
-        assert_routing_weights(ids, wts, logits, rep, run.M, st.L, what=tag)
-        c.update(assert_kv_rows(st, rep, pos, rps, what=f"full depth {tag}"))
+        assert_routing_weights(ids, wts, logits, rep, M, st.L, what=tag)
+        c.update(assert_kv_rows(st, rep, pos, rps, what=f"full depth {tag}", seq0=seq0))
         _say(f"full depth {tag} {c} forced={rep['forced']}")
 
     hid = st.hidden(0)
@@ -450,3 +456,19 @@ def test_attn92_full_depth_batch1_batch8_and_verify8(env):
         check("verify 1 x 8", ov, hv.cpu().numpy(), pv, rv, 8, kvv)
     finally:
         rv.close()
+    del kvv
+    # verify: 8 rows of each of the 8 sequences in one launch; sequence 5
+    s5 = 5
+    p64 = [w8.past + r for _ in range(8) for r in range(8)]
+    kv5 = [tuple(x[s5:s5 + 1].copy() for x in st.host_kv(l)) for l in range(st.L)]
+    r64 = GpuRun(st, rows=64, rows_per_seq=8)
+    try:
+        assert mk.mk_get_info(r64.h).launches_per_step == 1
+        h64 = st.hidden(2, rows=64)
+        o64 = r64.step(h64, p64).clone()
+        rows5 = slice(8 * s5, 8 * s5 + 8)
+        check("verify 8 x 8, sequence 5", o64[rows5], h64[rows5].cpu().numpy(), p64[rows5], r64, 8, kv5,
+              rows=rows5, seq0=s5)
+        assert torch.isfinite(o64).all()
+    finally:
+        r64.close()
