@@ -51,8 +51,12 @@ def log(msg):
 
 
 def source_hash():
+    """Hash of the decode kernel's sources (the mk_* files): counter records
+    taken on other sources are not reported."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "moe_layer_stack_amd", "csrc"))):
+        if not f.startswith("mk_"):
+            continue
         with open(os.path.join(ROOT, "moe_layer_stack_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -70,8 +70,10 @@ def lib():
                                   C.POINTER(C.c_int32), C.POINTER(KV), C.POINTER(C.c_float),
                                   C.POINTER(C.c_float), dp, ip, dp, dp]
         L.orc_set_threads.argtypes = [C.c_int]
+        L.orc_mla_attention.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_double,
+                                        dp, C.POINTER(C.c_uint16), C.POINTER(C.c_int32), dp]
         for f in ("orc_attn_block", "orc_route", "orc_moe_block", "orc_forward", "orc_num_threads",
-                  "orc_set_threads"):
+                  "orc_set_threads", "orc_mla_attention"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -297,3 +299,21 @@ def forward(dims, layers, hidden_in, positions=None, kvs=None, rows_per_seq=1):
                              hin.ctypes.data_as(C.POINTER(C.c_float)), out.ctypes.data_as(C.POINTER(C.c_float)),
                              _dp(logits), _ip(ids), _dp(w), _dp(margin)), "forward")
     return out, dict(logits=logits, ids=ids, w=w, margin=margin)
+
+
+def mla_attention(q, cache, positions, latent_dim, scale, rows_per_seq=1):
+    """MLA attention at decode over a latent cache (orc_mla_attention):
+    q [M][H][Dc + Dr] (float64), cache [n_seq][capacity][Dc + Dr] bf16 bits
+    (uint16), positions [M]; returns out [M][H][Dc] float64."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    cache = np.ascontiguousarray(cache, dtype=np.uint16)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    M, H, Dk = q.shape
+    n_seq, cap, Dk2 = cache.shape
+    if Dk2 != Dk or not 0 < latent_dim <= Dk:
+        raise ValueError("q and cache rows differ in width, or latent_dim is out of range")
+    out = np.empty((M, H, latent_dim), dtype=np.float64)
+    _check(lib().orc_mla_attention(M, rows_per_seq, H, latent_dim, Dk - latent_dim, n_seq, cap, float(scale), _dp(q),
+                                   cache.ctypes.data_as(C.POINTER(C.c_uint16)),
+                                   pos.ctypes.data_as(C.POINTER(C.c_int32)), _dp(out)), "mla_attention")
+    return out

@@ -375,3 +375,34 @@ int orc_forward(const orc_dims* dm, int L, const orc_layer* layers, int M, int r
   free(mg);
   return rc;
 }
+
+/* MLA attention at decode over the latent cache (definition in oracle.h):
+ * per row and head, the scores over positions 0..pos, their softmax, and the
+ * softmax-weighted sum of the latent part of the cache rows. */
+int orc_mla_attention(int M, int rows_per_seq, int H, int Dc, int Dr, int n_seq, int capacity, double scale,
+                      const double* q, const uint16_t* cache, const int32_t* positions, double* out) {
+  if (M <= 0 || rows_per_seq <= 0 || H <= 0 || Dc <= 0 || Dr < 0 || capacity <= 0) return ORC_EARG;
+  const int Dk = Dc + Dr;
+  for (int r = 0; r < M; ++r)
+    if (r / rows_per_seq >= n_seq || positions[r] < 0 || positions[r] >= capacity) return ORC_EPOS;
+#pragma omp parallel for schedule(static)
+  for (int rh = 0; rh < M * H; ++rh) {
+    const int r = rh / H, h = rh % H;
+    const int seq = r / rows_per_seq, npos = positions[r] + 1;
+    const double* qv = q + ((size_t)r * H + h) * Dk;
+    const uint16_t* rows = cache + (size_t)seq * capacity * Dk;
+    double* s = (double*)malloc(sizeof(double) * (size_t)npos);
+    for (int j = 0; j < npos; ++j) {
+      double dot = 0.0;
+      for (int i = 0; i < Dk; ++i) dot += qv[i] * orc_bf16_to_double(rows[(size_t)j * Dk + i]);
+      s[j] = scale * dot;
+    }
+    orc_softmax(npos, s, s);
+    double* o = out + ((size_t)r * H + h) * Dc;
+    for (int i = 0; i < Dc; ++i) o[i] = 0.0;
+    for (int j = 0; j < npos; ++j)
+      for (int i = 0; i < Dc; ++i) o[i] += s[j] * orc_bf16_to_double(rows[(size_t)j * Dk + i]);
+    free(s);
+  }
+  return ORC_OK;
+}

@@ -135,6 +135,24 @@ int orc_forward(const orc_dims* dm, int L, const orc_layer* layers, int M, int r
                 const int32_t* positions, orc_kv* kv, const float* hidden_in, float* hidden_out,
                 double* t_logits, int* t_ids, double* t_w, double* t_margin);
 
+/* ---- multi-head latent attention (MLA) at decode, absorbed form ----
+ * The pages name MLA as the attention of the model (P4, paragraph on VMEM
+ * budgeting: the KV cache MLA uses is short-lived) and define nothing else;
+ * the definition followed is the published one (multi-head latent
+ * attention, DeepSeek-V2 report, section 2.1): a cache row per position is
+ * a compressed latent c (Dc values) and one rotary key k_R (Dr values)
+ * shared by all heads; head h's key is (W_UK,h c, k_R) and its value
+ * W_UV,h c.  At decode the up-projections fold into the query and the
+ * output, so the attention itself runs over the cache rows directly:
+ *   q[r][h]  = (W_UK,h^T q_nope, q_rope)   (Dc + Dr values, given)
+ *   s_j      = scale * q[r][h] . cache[seq][j],   j = 0 .. positions[r]
+ *   a        = softmax(s)
+ *   out[r][h][i] = sum_j a_j cache[seq][j][i],   i < Dc
+ * (the head's output is then W_UV,h out[r][h]).  Row r belongs to sequence
+ * r / rows_per_seq; cache is bf16 [n_seq][capacity][Dc + Dr]. */
+int orc_mla_attention(int M, int rows_per_seq, int H, int Dc, int Dr, int n_seq, int capacity, double scale,
+                      const double* q, const uint16_t* cache, const int32_t* positions, double* out);
+
 /* threads the oracle's parallel loops use (1 when built without OpenMP) */
 int orc_num_threads(void);
 int orc_set_threads(int n);

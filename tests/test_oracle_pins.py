@@ -632,3 +632,113 @@ def test_moe_norm_uses_its_own_gain(orc):
     out_m, _ = orc.forward(dims_m, [ly], h)
     np.testing.assert_array_equal(out_a, out_m)
     assert not np.array_equal(out_m, h)
+
+
+# ---------------------------------------------------------------- MLA attention
+# The reading: multi-head latent attention as published (DeepSeek-V2 report,
+# section 2.1), in the absorbed form a decode step uses (oracle.h).
+
+
+def _bf16_random(rng, shape, scale=1.0):
+    """bf16 bit patterns of N(0, scale^2) draws (truncated float32: exact values)."""
+    a = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _mha_row(q_nope, q_rope, c, k_r, W_uk, W_uv, scale):
+    """Textbook attention of one head over explicit keys and values built from
+    the latents: key_j = (W_uk c_j, k_r_j), value_j = W_uv c_j."""
+    keys = np.concatenate([c @ W_uk.T, k_r], axis=1)  # [P][d_nope + Dr]
+    vals = c @ W_uv.T                                  # [P][d_v]
+    s = scale * (keys @ np.concatenate([q_nope, q_rope]))
+    a = np.exp(s - s.max())
+    a /= a.sum()
+    return a @ vals
+
+
+def test_mla_absorbed_equals_explicit_heads(orc):
+    """The absorbed form over the latent cache, projected by W_UV, equals
+    per-head attention over explicitly decompressed keys and values (the
+    identity MLA decode rests on).  Catches a dropped rotary part of the
+    score, a wrong scale, values that include the rotary columns, and an
+    off-by-one in the attended range."""
+    rng = np.random.default_rng(11)
+    H, Dc, Dr, dn, dv, n_seq, cap = 3, 24, 8, 12, 10, 2, 11
+    cache = _bf16_random(rng, (n_seq, cap, Dc + Dr))
+    cf = _bf16_to_f64(cache)
+    W_uk = rng.standard_normal((H, dn, Dc)) * 0.3
+    W_uv = rng.standard_normal((H, dv, Dc)) * 0.3
+    positions = [4, 10, 0, 7]  # rows 0, 1 in sequence 0; rows 2, 3 in sequence 1
+    rps, scale = 2, 1.0 / math.sqrt(dn + Dr)
+    q_nope = rng.standard_normal((len(positions), H, dn))
+    q_rope = rng.standard_normal((len(positions), H, Dr))
+    q = np.concatenate([np.einsum("hnc,rhn->rhc", W_uk, q_nope), q_rope], axis=2)
+    out = orc.mla_attention(q, cache, positions, Dc, scale, rows_per_seq=rps)
+    for r, p in enumerate(positions):
+        seq = r // rps
+        c, k_r = cf[seq, :p + 1, :Dc], cf[seq, :p + 1, Dc:]
+        for h in range(H):
+            want = _mha_row(q_nope[r, h], q_rope[r, h], c, k_r, W_uk[h], W_uv[h], scale)
+            np.testing.assert_allclose(W_uv[h] @ out[r, h], want, rtol=1e-11, atol=1e-12)
+
+
+def test_mla_zero_query_averages_the_latents(orc):
+    """q = 0: every score is 0, the weights are uniform over positions
+    0..pos, and the output is the mean of those latents (closed form).
+    Catches a softmax over the whole capacity or including position pos + 1."""
+    rng = np.random.default_rng(12)
+    Dc, Dr, cap = 16, 4, 9
+    cache = _bf16_random(rng, (1, cap, Dc + Dr))
+    cf = _bf16_to_f64(cache)
+    for p in (0, 3, cap - 1):
+        out = orc.mla_attention(np.zeros((1, 2, Dc + Dr)), cache, [p], Dc, 0.7)
+        want = cf[0, :p + 1, :Dc].mean(axis=0)
+        np.testing.assert_allclose(out[0, 0], want, rtol=1e-14, atol=1e-15)
+        np.testing.assert_array_equal(out[0, 0], out[0, 1])
+
+
+def test_mla_first_position_returns_its_latent(orc):
+    """At position 0 the only weight is 1: the output is the latent part of
+    cache row 0 exactly, whatever the query."""
+    rng = np.random.default_rng(13)
+    Dc, Dr = 16, 4
+    cache = _bf16_random(rng, (1, 5, Dc + Dr))
+    out = orc.mla_attention(rng.standard_normal((1, 3, Dc + Dr)) * 5, cache, [0], Dc, 1.3)
+    for h in range(3):
+        np.testing.assert_array_equal(out[0, h], _bf16_to_f64(cache)[0, 0, :Dc])
+
+
+def test_mla_reads_no_position_after_its_own(orc):
+    """Cache rows after a row's position do not change its output (bitwise);
+    the row at its position does."""
+    rng = np.random.default_rng(14)
+    Dc, Dr, cap, p = 16, 4, 12, 6
+    cache = _bf16_random(rng, (1, cap, Dc + Dr))
+    q = rng.standard_normal((1, 2, Dc + Dr))
+    base = orc.mla_attention(q, cache, [p], Dc, 0.5)
+    later = cache.copy()
+    later[0, p + 1:] = _bf16_random(rng, (cap - p - 1, Dc + Dr))
+    np.testing.assert_array_equal(orc.mla_attention(q, later, [p], Dc, 0.5), base)
+    own = cache.copy()
+    own[0, p] = _bf16_random(rng, (Dc + Dr,))
+    assert not np.array_equal(orc.mla_attention(q, own, [p], Dc, 0.5), base)
+
+
+def test_mla_dominant_score_selects_its_row(orc):
+    """A query aligned with one cache row and a large scale: that row's weight
+    is 1 to double precision, so the output is its latent (the softmax is
+    taken with the maximum subtracted; without it the exponentials overflow)."""
+    rng = np.random.default_rng(15)
+    Dc, Dr, cap, p, j = 16, 4, 10, 8, 5
+    cache = _bf16_random(rng, (1, cap, Dc + Dr))
+    cf = _bf16_to_f64(cache)
+    q = cf[0, j][None, None, :] * 1.0
+    gaps = cf[0, j] @ cf[0, j] - cf[0, :p + 1] @ cf[0, j]
+    gaps[j] = np.inf
+    scale = 800.0 / gaps.min()  # every other score is at least 800 below row j's
+    out = orc.mla_attention(q, cache, [p], Dc, scale)
+    np.testing.assert_allclose(out[0, 0], cf[0, j, :Dc], rtol=0, atol=1e-12 * np.abs(cf[0, j, :Dc]).max())
