@@ -1,4 +1,4 @@
-"""Compile libmk.so (the persistent decode kernel and its C ABI) for gfx950."""
+"""Compile libmk.so (the persistent decode kernel, the MLA attention kernels and their C ABI) for gfx950."""
 import os
 import subprocess
 
@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["mk_kernel.hip", "mk_runtime.hip"]
+SOURCES = ["mk_kernel.hip", "mk_runtime.hip", "mla.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wall", "-Wno-unused-function"]

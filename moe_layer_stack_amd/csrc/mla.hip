@@ -1,0 +1,387 @@
+// mla.hip -- multi-head latent attention (MLA) at decode over a latent KV
+// cache (include/mk_mla.h): the split launch on the matrix cores and the
+// combine launch, and their C ABI.
+//
+// Definition (absorbed form of the published MLA, DeepSeek-V2 report,
+// section 2.1; the pages only name MLA, P4 paragraph on VMEM budgeting): row
+// r, head h attends the cache rows 0 .. positions[r] of its sequence with
+// scores scale * q . row and returns the softmax-weighted sum of the rows'
+// first 512 (latent) columns.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "mk_mla.h"
+
+namespace mla {
+
+constexpr int kDc = 512;                         // latent columns (the values)
+constexpr int kDr = 64;                          // rotary key columns
+constexpr int kDk = kDc + kDr;                   // a cache row: the key
+constexpr int kRowBytes = kDk * 2;               // 1152 bytes of bf16
+constexpr int kTile = 16;                        // positions per tile
+constexpr int kTileU4 = kTile * kRowBytes / 16;  // 16-byte pieces of a tile (1152)
+constexpr int kRowU4 = kRowBytes / 16;           // 72 per row
+// LDS row pitch: 1152 bytes is 288 dwords, which would put all 16 rows of a
+// matrix-core read on the same banks; 16 bytes of padding spread them.
+constexpr int kPitch = kRowBytes + 16;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kQ = 16;                // query vectors per workgroup: one matrix-core operand
+constexpr int kChunks = kDk / 32;     // 18 key chunks of 32 columns
+constexpr int kMaxChunks = 5;         // waves take 5, 5, 4 and 4 chunks
+constexpr int kVals = kDc / kWaves;   // latent columns per wave (128)
+constexpr int kPartStride = 4 + kDc;  // floats per query of a split partial: m, l, -, -, acc[512]
+constexpr int kLoads = (kTileU4 + kThreads - 1) / kThreads;  // 16-byte loads per thread per tile (5)
+static_assert(kChunks == 2 * kMaxChunks + 2 * (kMaxChunks - 1), "chunk split");
+
+struct Params {
+  const float* q;            // [M][H][kDk]
+  const uint16_t* cache;     // [n_seq][cap][kDk]
+  const int32_t* positions;  // [M]
+  float* out;                // [M][H][kDc]
+  float* part;               // [n_seq_step][QG][S][kQ][kPartStride]
+  unsigned* err;             // set when a position is outside the cache
+  int M, H, rps, cap, QG, S;
+  float qscale;              // scale * log2(e): scores in base-2 exponent units
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const_cast<char*>(p)));
+}
+__device__ __forceinline__ short bf16_bits(__bf16 h) { return __builtin_bit_cast(short, h); }
+
+// A tile of 16 cache rows in flight through registers: piece u = thread +
+// 256k of the tile (row u / 72, 16 bytes at u % 72).  Rows past the capacity
+// re-read the last row (their scores are masked).
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+struct Prefetch {
+  u32x4_t v[kLoads];
+};
+__device__ __forceinline__ void load_tile(Prefetch& pf, const uint16_t* rows, int t, int cap) {
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) {
+    const int u = min((int)threadIdx.x + k * kThreads, kTileU4 - 1);
+    const int r = min(t * kTile + u / kRowU4, cap - 1);
+    pf.v[k] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(rows + (size_t)r * kDk) + (u % kRowU4) * 16);
+  }
+}
+__device__ __forceinline__ void store_tile(const Prefetch& pf, char* tile) {
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) {
+    const int u = (int)threadIdx.x + k * kThreads;
+    if (u < kTileU4) *reinterpret_cast<u32x4_t*>(tile + (u / kRowU4) * kPitch + (u % kRowU4) * 16) = pf.v[k];
+  }
+}
+
+// Workgroup (seq, qg, s): the 16 query vectors qg*16 .. qg*16+15 of sequence
+// seq (query i of a sequence is row i / H, head i % H; H is a multiple of
+// 16, so the 16 share one row and one position) against split s of the
+// row's positions, tiles of 16 positions.
+__global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char tile[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) f32x4_t exch[kWaves][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int s = blockIdx.x % p.S, qg = (blockIdx.x / p.S) % p.QG, seq = blockIdx.x / (p.S * p.QG);
+  const int row = seq * p.rps + (qg * kQ) / p.H;
+  const int pos = p.positions[row];
+  const bool ok = pos >= 0 && pos < p.cap;
+  if (!ok && threadIdx.x == 0 && s == 0) __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int npos = ok ? pos + 1 : 0;
+  const int ntile = (npos + kTile - 1) / kTile;
+  const int t_lo = (int)(((long long)s * ntile) / p.S), t_hi = (int)(((long long)(s + 1) * ntile) / p.S);
+  const uint16_t* rows = p.cache + (size_t)seq * p.cap * kDk;
+  const int qq = lane & 15, lg = lane >> 4;
+  // This wave's key chunks and its query operand for them, lane l: query
+  // l & 15, columns 32c + 8(l >> 4) .. +7, bf16 high and low parts.
+  const int c0 = wave < 2 ? kMaxChunks * wave : 2 * kMaxChunks + (kMaxChunks - 1) * (wave - 2);
+  const int nc = wave < 2 ? kMaxChunks : kMaxChunks - 1;
+  bf16x8_t qh[kMaxChunks], ql[kMaxChunks];
+  {
+    const float* src = p.q + ((size_t)row * p.H + (qg * kQ) % p.H + qq) * kDk + lg * 8;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int cc = c0 + (c < nc ? c : 0);
+      const float4 a0 = *reinterpret_cast<const float4*>(src + cc * 32);
+      const float4 a1 = *reinterpret_cast<const float4*>(src + cc * 32 + 4);
+      const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = x[j] * p.qscale;
+        const __bf16 hi = (__bf16)v;
+        qh[c][j] = hi;
+        ql[c][j] = (__bf16)(v - (float)hi);
+      }
+    }
+  }
+  Prefetch pf;
+  f32x4_t acc[kVals / 16];
+#pragma unroll
+  for (int nb = 0; nb < kVals / 16; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_l = -INFINITY, lsum = 0.f;
+  if (t_lo < t_hi) {
+    load_tile(pf, rows, t_lo, p.cap);
+    store_tile(pf, tile);
+  }
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; ++t) {
+    // the next tile (at the last one, this one again) lands while this one is used
+    load_tile(pf, rows, min(t + 1, t_hi - 1), p.cap);
+    // partial scores over this wave's chunks: D lane l = positions 4(l>>4)+i, query l&15
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const char* kr = tile + qq * kPitch + lg * 16;
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c) {
+        if (c < nc) {
+          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kr + (c0 + c) * 64));
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[c], sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[c], sc, 0, 0, 0);
+        }
+      }
+    }
+    exch[wave][lane] = sc;
+    __syncthreads();
+    // full scores: the four waves' partials in a fixed order (every wave
+    // then holds the same values)
+    float sv[4];
+    {
+      f32x4_t tot = exch[0][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) tot += exch[w][lane];
+      bool up = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jpos = t * kTile + 4 * lg + i;
+        sv[i] = jpos < npos ? tot[i] : -INFINITY;
+        up |= sv[i] > m_l + 8.f;
+      }
+      // online softmax in base 2 with a reference maximum that is raised
+      // only when a score exceeds it by more than 8 (2^8 stays exact enough
+      // in fp32); wave-uniform
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m_l + 8.f;
+        const float corr = !raise ? 1.f : (m_l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_l - mx);
+        lsum *= corr;
+#pragma unroll
+        for (int nb = 0; nb < kVals / 16; ++nb) acc[nb] *= corr;
+        m_l = raise ? mx : m_l;
+      }
+    }
+    s16x4_t ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_l);
+      lsum += pv;
+      const __bf16 h = (__bf16)pv;
+      ph[i] = bf16_bits(h);
+      pl[i] = bf16_bits((__bf16)(pv - (float)h));
+    }
+    // this wave's 128 latent columns: V^T operand by transpose loads, lane
+    // 16g + 4j + c reads position 4g + j, columns 128w + 16nb + 4c .. +3
+    {
+      const char* vr = tile + (4 * lg + ((lane >> 2) & 3)) * kPitch + wave * kVals * 2 + (lane & 3) * 8;
+#pragma unroll
+      for (int nb = 0; nb < kVals / 16; ++nb) {
+        const s16x4_t vt = lds_read_tr16(vr + nb * 32);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, acc[nb], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with the tile and the exchange slots
+    store_tile(pf, tile);
+    __syncthreads();
+  }
+  // the split's partial: m (natural units), l, and the sums, query-major
+  float lw = lsum;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+  constexpr float kLn2 = 0.6931471805599453f;
+  float* dst = p.part + ((size_t)((seq * p.QG + qg) * p.S + s) * kQ + qq) * kPartStride;
+#pragma unroll
+  for (int nb = 0; nb < kVals / 16; ++nb)
+    *reinterpret_cast<float4*>(dst + 4 + wave * kVals + nb * 16 + 4 * lg) =
+        make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+  if (wave == 0 && lg == 0) {
+    dst[0] = m_l == -INFINITY ? -INFINITY : m_l * kLn2;
+    dst[1] = lw;
+  }
+}
+
+// out[r][h][:] from the S split partials of its query: weights e^(m_s - max)
+// over the splits, in split order; a row whose position was rejected gets 0.
+__global__ void __launch_bounds__(128) combine_kernel(Params p) {
+  const int r = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int seq = r / p.rps, qi = (r % p.rps) * p.H + h;
+  const int qg = qi / kQ, q = qi % kQ;
+  const float* base = p.part + ((size_t)((seq * p.QG + qg) * p.S) * kQ + q) * kPartStride;
+  const size_t sstride = (size_t)kQ * kPartStride;
+  float M = -INFINITY;
+  for (int s = 0; s < p.S; ++s) M = fmaxf(M, base[s * sstride]);
+  float L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int d = threadIdx.x * 4;
+  for (int s = 0; s < p.S; ++s) {
+    const float* b = base + s * sstride;
+    const float w = b[0] == -INFINITY ? 0.f : __expf(b[0] - M);
+    L = fmaf(w, b[1], L);
+    const float4 a = *reinterpret_cast<const float4*>(b + 4 + d);
+    o.x = fmaf(w, a.x, o.x); o.y = fmaf(w, a.y, o.y); o.z = fmaf(w, a.z, o.z); o.w = fmaf(w, a.w, o.w);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<float4*>(p.out + ((size_t)r * p.H + h) * kDc + d) =
+      make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+}
+
+}  // namespace mla
+
+struct mk_mla_handle {
+  mk_mla_config cfg;
+  int device;
+  int QG, S, n_seq_step;
+  float* part;
+  unsigned* err;
+  size_t part_bytes;
+};
+
+namespace {
+
+thread_local std::string g_mla_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_mla_error = buf;
+  return status;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_mla_last_error(void) { return g_mla_error.c_str(); }
+
+int mk_mla_create(const mk_mla_config* cfg, mk_mla_handle** out) {
+  using namespace mla;
+  if (!cfg || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  const mk_mla_config c = *cfg;
+  if (c.rows < 1 || c.rows_per_seq < 1 || c.rows % c.rows_per_seq != 0 || c.n_seq < c.rows / c.rows_per_seq ||
+      c.capacity < 1 || !(c.scale > 0.f) || !std::isfinite(c.scale) || c.n_heads < 1)
+    return fail(MK_ERR_INVALID_ARG, "inconsistent config (rows %d, rows_per_seq %d, n_seq %d, capacity %d, scale %g)",
+                c.rows, c.rows_per_seq, c.n_seq, c.capacity, (double)c.scale);
+  if (c.latent_dim != kDc || c.rope_dim != kDr)
+    return fail(MK_ERR_UNSUPPORTED, "latent_dim %d / rope_dim %d: the kernel is built for %d / %d", c.latent_dim,
+                c.rope_dim, kDc, kDr);
+  if (c.n_heads % kQ != 0 || c.n_heads > 128 || c.rows > 64)
+    return fail(MK_ERR_UNSUPPORTED, "n_heads %d (16, 32, 64 or 128) or rows %d (<= 64) out of range", c.n_heads,
+                c.rows);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MK_ERR_DEVICE, "no HIP device");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MK_ERR_DEVICE, "hipGetDeviceProperties failed");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MK_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  mk_mla_handle* h = new (std::nothrow) mk_mla_handle();
+  if (!h) return fail(MK_ERR_HIP, "out of host memory");
+  h->cfg = c;
+  h->device = dev;
+  h->n_seq_step = c.rows / c.rows_per_seq;
+  h->QG = c.n_heads * c.rows_per_seq / kQ;
+  // splits: about two workgroups per CU, each with at least one tile
+  const int base = h->n_seq_step * h->QG;
+  const int want = (2 * prop.multiProcessorCount + base - 1) / base;
+  const int tiles = (c.capacity + kTile - 1) / kTile;
+  h->S = want < 1 ? 1 : (want > tiles ? tiles : want);
+  h->part_bytes = (size_t)base * h->S * kQ * kPartStride * sizeof(float);
+  if (hipMalloc(&h->part, h->part_bytes) != hipSuccess) {
+    delete h;
+    return fail(MK_ERR_HIP, "hipMalloc of %zu bytes failed", h->part_bytes);
+  }
+  if (hipMalloc(&h->err, 256) != hipSuccess || hipMemset(h->err, 0, 256) != hipSuccess) {
+    (void)hipFree(h->part);
+    delete h;
+    return fail(MK_ERR_HIP, "hipMalloc of the error word failed");
+  }
+  *out = h;
+  return MK_OK;
+}
+
+int mk_mla_attention(mk_mla_handle* h, const float* q, const uint16_t* cache, const int32_t* positions, float* out,
+                     void* stream) {
+  using namespace mla;
+  if (!h || !q || !cache || !positions || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return fail(MK_ERR_INVALID_ARG, "current device differs from the handle's device");
+  const mk_mla_config& c = h->cfg;
+  Params p{};
+  p.q = q;
+  p.cache = cache;
+  p.positions = positions;
+  p.out = out;
+  p.part = h->part;
+  p.err = h->err;
+  p.M = c.rows;
+  p.H = c.n_heads;
+  p.rps = c.rows_per_seq;
+  p.cap = c.capacity;
+  p.QG = h->QG;
+  p.S = h->S;
+  p.qscale = c.scale * 1.4426950408889634f;
+  const hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(split_kernel, dim3(h->n_seq_step * h->QG * h->S), dim3(kThreads), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MK_ERR_HIP, "split launch failed: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(combine_kernel, dim3(c.rows * c.n_heads), dim3(128), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(MK_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  return MK_OK;
+}
+
+int mk_mla_sync(mk_mla_handle* h, void* stream) {
+  if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
+  const hipStream_t st = (hipStream_t)stream;
+  unsigned flag = 0;
+  if (hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpy(&flag, h->err, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(MK_ERR_HIP, "synchronising the stream failed");
+  if (flag) {
+    if (hipMemset(h->err, 0, sizeof flag) != hipSuccess) return fail(MK_ERR_HIP, "clearing the error word failed");
+    return fail(MK_ERR_INVALID_ARG, "a row's position was outside [0, capacity %d)", h->cfg.capacity);
+  }
+  return MK_OK;
+}
+
+int mk_mla_get_info(const mk_mla_handle* h, mk_mla_info* info) {
+  if (!h || !info) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  info->splits = h->S;
+  info->workgroups = h->n_seq_step * h->QG * h->S;
+  info->workspace_bytes = (int64_t)(h->part_bytes + 256);
+  return MK_OK;
+}
+
+int mk_mla_destroy(mk_mla_handle* h) {
+  if (!h) return MK_OK;
+  (void)hipFree(h->part);
+  (void)hipFree(h->err);
+  delete h;
+  return MK_OK;
+}
+
+}  // extern "C"

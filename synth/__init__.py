@@ -22,6 +22,7 @@ F32, BF16 = 0, 1
 K_G1, K_WQ, K_WK, K_WV, K_WO, K_G2, K_WR, K_BR = 1, 2, 3, 4, 5, 6, 7, 8
 K_WGATE, K_WUP, K_WDOWN, K_SGATE, K_SUP, K_SDOWN = 9, 10, 11, 12, 13, 14
 K_HIDDEN, K_KCACHE, K_VCACHE = 20, 21, 22
+K_MLA_CACHE, K_MLA_Q = 23, 24  # latent cache rows and absorbed queries of the MLA attention
 
 _lib = None
 

@@ -1,5 +1,6 @@
 """The C ABI on the CPU: the library loads, exports every function that
-include/mk.h declares, and rejects bad arguments before touching a device."""
+include/mk.h and include/mk_mla.h declare, and rejects bad arguments before
+touching a device."""
 import ctypes as C
 import os
 import re
@@ -32,6 +33,36 @@ def test_every_declared_function_is_exported(mk):
     for n in names:
         assert hasattr(L, n), n
     assert set(mk.EXPORTS) == names
+
+
+def test_every_declared_mla_function_is_exported(mk):
+    from moe_layer_stack_amd import mla
+    names = declared("mk_mla.h")
+    assert {"mk_mla_create", "mk_mla_attention", "mk_mla_destroy"} <= names
+    L = C.CDLL(os.path.join(ROOT, "moe_layer_stack_amd", "libmk.so"))
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(mla.MLA_EXPORTS) == names
+    # mk_mla_config: 7 int32 + 1 float; mk_mla_info: 2 int32 + 1 int64
+    assert C.sizeof(mla.mk_mla_config) == 32
+    assert C.sizeof(mla.mk_mla_info) == 16
+
+
+def test_mla_create_rejects_bad_configs_before_the_device(mk):
+    from moe_layer_stack_amd import mla
+    L = mla.lib()
+    h = C.c_void_p()
+    assert L.mk_mla_create(None, C.byref(h)) == mk.MK_ERR_INVALID_ARG
+    good = dict(n_heads=64, latent_dim=512, rope_dim=64, rows=8, rows_per_seq=1, n_seq=8, capacity=4160, scale=0.072)
+    for bad, want in ((dict(rows=0), mk.MK_ERR_INVALID_ARG), (dict(rows_per_seq=3), mk.MK_ERR_INVALID_ARG),
+                      (dict(n_seq=4), mk.MK_ERR_INVALID_ARG), (dict(scale=0.0), mk.MK_ERR_INVALID_ARG),
+                      (dict(scale=float("nan")), mk.MK_ERR_INVALID_ARG), (dict(latent_dim=256), mk.MK_ERR_UNSUPPORTED),
+                      (dict(rope_dim=32), mk.MK_ERR_UNSUPPORTED), (dict(n_heads=8), mk.MK_ERR_UNSUPPORTED),
+                      (dict(n_heads=256), mk.MK_ERR_UNSUPPORTED), (dict(rows=72, n_seq=72), mk.MK_ERR_UNSUPPORTED)):
+        cfg = mla.mk_mla_config(**{**good, **bad})
+        assert L.mk_mla_create(C.byref(cfg), C.byref(h)) == want, bad
+        assert h.value is None
+    assert L.mk_mla_destroy(None) == mk.MK_OK
 
 
 def test_synth_exports(syn):

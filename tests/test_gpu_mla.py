@@ -1,0 +1,174 @@
+"""MLA attention at decode (include/mk_mla.h) through the C ABI against the
+oracle's absorbed-form definition on the same seeded inputs: one decode row,
+8 sequences at ragged positions (0 and the last cache slot included), verify
+rows, every head count the kernel takes, a capacity that is not a multiple of
+the 16-position tile, a sharp softmax, the 64-row verify shape, repeatability,
+and a rejected position.
+
+Bar, from the arithmetic: queries and softmax weights enter the matrix cores
+as bf16 high and low parts (relative error about 2^-17 each), the cache is
+bf16 exactly and every sum is fp32 over at most 4160 positions, so the
+outputs (convex combinations of N(0, 1) latents, |out| < 5) carry errors of
+order 1e-6 relative; the bound below leaves a factor of about 7 over the
+worst case measured (max |d| 7e-5 with a sharp softmax) and is 20-50 times
+tighter than the stated bf16 / fp32-accumulate tolerance for the step's
+hidden state (max |d| 2e-2, relative L2 5e-3)."""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"max_abs": 1e-3, "rel_l2": 1e-4}
+DC, DR = 512, 64
+SCALE = 1.0 / math.sqrt(128 + DR)  # 1/sqrt(d_nope + Dr) of the published model
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_layer_stack_amd as mk
+    mk.lib()
+    return torch
+
+
+def _inputs(torch, H, rows, n_seq, cap, seed, q_std):
+    """Cache rows N(0, 1) in bf16 and queries N(0, q_std^2) in fp32, seeded."""
+    import synth
+    cache = torch.empty(n_seq, cap, DC + DR, dtype=torch.bfloat16, device="cuda")
+    synth.device_normal(cache.data_ptr(), cache.numel(), synth.BF16, seed, synth.stream_id(-1, synth.K_MLA_CACHE))
+    q = torch.empty(rows, H, DC + DR, dtype=torch.float32, device="cuda")
+    synth.device_normal(q.data_ptr(), q.numel(), synth.F32, seed, synth.stream_id(-1, synth.K_MLA_Q), 0.0, q_std)
+    return q, cache
+
+
+def _host_bits(cache):
+    """bf16 cache as its bit patterns on the host."""
+    import torch
+    return cache.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _run(torch, H, positions, rps, n_seq, cap, seed=7, scale=SCALE, q_std=0.25, calls=1):
+    from moe_layer_stack_amd import mla
+    rows = len(positions)
+    cfg = mla.mk_mla_config(n_heads=H, latent_dim=DC, rope_dim=DR, rows=rows, rows_per_seq=rps, n_seq=n_seq,
+                            capacity=cap, scale=scale)
+    h = mla.mk_mla_create(cfg)
+    try:
+        info = mla.mk_mla_get_info(h)
+        q, cache = _inputs(torch, H, rows, n_seq, cap, seed, q_std)
+        pos = torch.tensor(positions, dtype=torch.int32, device="cuda")
+        outs = []
+        for _ in range(calls):
+            out = torch.full((rows, H, DC), float("nan"), dtype=torch.float32, device="cuda")
+            mla.mk_mla_attention(h, q.data_ptr(), cache.data_ptr(), pos.data_ptr(), out.data_ptr(), 0)
+            rc = mla.mk_mla_sync(h, 0)
+            outs.append((out, rc))
+        return outs, q, cache, info
+    finally:
+        mla.mk_mla_destroy(h)
+
+
+def _check(out, q, cache, positions, rps, scale, what, rows=None, seq0=0):
+    """out (rows given, default all) against the oracle walked over the same bytes."""
+    import oracle
+    rows = list(range(len(positions))) if rows is None else list(rows)
+    nseq = (max(rows) // rps) - seq0 + 1
+    bits = _host_bits(cache)[seq0:seq0 + nseq]
+    ref = oracle.mla_attention(q[rows].cpu().numpy().astype(np.float64), bits, [positions[r] for r in rows], DC, scale,
+                               rows_per_seq=rps)
+    got = out[rows].cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), what
+    err = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    _say(f"{what}: max|d| {err:.3g}, rel-L2 {rel:.3g}, max|ref| {np.abs(ref).max():.3g}")
+    assert err <= TOL["max_abs"], f"{what}: max|d| {err}"
+    assert rel <= TOL["rel_l2"], f"{what}: rel-L2 {rel}"
+
+
+def test_mla_decode_one_row(env):
+    torch = env
+    pos = [4096]
+    _say("MLA H=64, 1 row at position 4096")
+    outs, q, cache, info = _run(torch, 64, pos, 1, 1, 4160)
+    (o, rc), = outs
+    assert rc == 0
+    _check(o, q, cache, pos, 1, SCALE, f"1 row, {info.splits} splits")
+
+
+def test_mla_decode_eight_sequences_ragged(env):
+    torch = env
+    pos = [0, 5, 31, 100, 1000, 2049, 4095, 4159]
+    _say(f"MLA H=64, 8 sequences at {pos}")
+    outs, q, cache, info = _run(torch, 64, pos, 1, 8, 4160)
+    (o, rc), = outs
+    assert rc == 0
+    _check(o, q, cache, pos, 1, SCALE, f"8 sequences ragged, {info.splits} splits")
+
+
+def test_mla_verify_rows(env):
+    torch = env
+    pos = [4096 + r for r in range(8)] + [100 + r for r in range(8)]
+    _say("MLA H=64, 2 sequences x 8 verify rows")
+    outs, q, cache, info = _run(torch, 64, pos, 8, 2, 4160)
+    (o, rc), = outs
+    assert rc == 0
+    _check(o, q, cache, pos, 8, SCALE, f"2 x 8 verify rows, {info.splits} splits")
+
+
+@pytest.mark.parametrize("H", [16, 32, 128])
+def test_mla_head_counts_and_ragged_capacity(env, H):
+    torch = env
+    pos = [999, 17]
+    _say(f"MLA H={H}, capacity 1000, positions {pos}")
+    outs, q, cache, info = _run(torch, H, pos, 1, 2, 1000)
+    (o, rc), = outs
+    assert rc == 0
+    _check(o, q, cache, pos, 1, SCALE, f"H={H}, capacity 1000")
+
+
+def test_mla_sharp_softmax(env):
+    """Scores spread over tens of units: the reference maximum is raised
+    inside the tile loop and the splits' maxima differ widely."""
+    torch = env
+    pos = [2047, 1024, 15, 16]
+    _say("MLA H=64, scale x 8, queries N(0, 0.5^2)")
+    outs, q, cache, info = _run(torch, 64, pos, 1, 4, 2048, scale=8 * SCALE, q_std=0.5)
+    (o, rc), = outs
+    assert rc == 0
+    _check(o, q, cache, pos, 1, 8 * SCALE, "sharp softmax")
+
+
+def test_mla_verify_64_rows_repeatable(env):
+    """8 sequences x 8 verify rows (the 64-row verify shape): sequences 0 and 5
+    against the oracle, and a second call equal bit for bit."""
+    torch = env
+    pos = [4096 + r for _ in range(8) for r in range(8)]
+    _say("MLA H=64, 8 sequences x 8 verify rows, two calls")
+    outs, q, cache, info = _run(torch, 64, pos, 8, 8, 4160, calls=2)
+    (o1, rc1), (o2, rc2) = outs
+    assert rc1 == 0 and rc2 == 0
+    assert torch.equal(o1, o2)
+    for s in (0, 5):
+        _check(o1, q, cache, pos, 8, SCALE, f"64 verify rows, sequence {s}", rows=range(8 * s, 8 * s + 8), seq0=s)
+
+
+def test_mla_rejected_position(env):
+    """A position at the capacity is not read: its row's outputs are zero,
+    the sync reports MK_ERR_INVALID_ARG once, and the other row is right."""
+    import moe_layer_stack_amd as mk
+    torch = env
+    pos = [10, 1000]
+    _say("MLA H=16, capacity 1000, position 1000 rejected")
+    outs, q, cache, info = _run(torch, 16, pos, 1, 2, 1000, calls=2)
+    for o, rc in outs:
+        assert rc == mk.MK_ERR_INVALID_ARG
+        assert (o[1] == 0).all()
+        _check(o, q, cache, pos, 1, SCALE, "row 0 beside a rejected row", rows=[0])
