@@ -22,7 +22,8 @@ verify pass (1 and 8 sequences x 8 rows); speculative decoding around the
 verify pass with a synthetic acceptance process (effective tokens/s at about
 6 tokens per step); the same step as one kernel launch per phase of every
 layer (the many-kernels baseline, batch 1 and 8, and at batch 1 replayed
-from a HIP graph); the 16-layer MoE-only stack at batch 1 and 8.
+from a HIP graph); the 16-layer MoE-only stack at batch 1 and 8; the MLA
+attention over a latent cache (include/mk_mla.h) at 1, 8 and 8 x 8 rows.
 
 HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
 this script with --calib-copy-mib, one with --pmc FETCH_SIZE and one with
@@ -262,6 +263,69 @@ def moe16_legs(torch, mk, steps, warmup):
     return out
 
 
+def mla_legs(torch, steps, warmup):
+    """MLA attention at decode over a latent cache (include/mk_mla.h; H=64
+    heads, latent 512 + rotary 64 per cache row, bf16): one call = the split
+    and combine launches.  Shapes: 1 sequence at 4096 past positions, 8
+    sequences, 8 sequences x 8 verify rows, and 1 sequence at 32768.  Each
+    timed call follows a 1 GiB device copy (outside the events) so the cache
+    is read from HBM; a back-to-back run is the control.  Bytes: the cache
+    rows read plus queries and outputs."""
+    import numpy as np
+    import synth
+    from moe_layer_stack_amd import mla
+    H, DK, DC = 64, mla.MLA_LATENT_DIM + mla.MLA_ROPE_DIM, mla.MLA_LATENT_DIM
+    n = (1 << 30) // 4
+    flush = (torch.ones(n, dtype=torch.float32, device="cuda"), torch.empty(n, dtype=torch.float32, device="cuda"))
+    out = {}
+    for name, rows, rps, n_seq, cap, p0 in (("mla_b1", 1, 1, 1, 4160, 4096), ("mla_b8", 8, 1, 8, 4160, 4096),
+                                             ("mla_verify64", 64, 8, 8, 4160, 4096),
+                                             ("mla_b1_32k", 1, 1, 1, 32832, 32768)):
+        cfg = mla.mk_mla_config(n_heads=H, latent_dim=DC, rope_dim=DK - DC, rows=rows, rows_per_seq=rps, n_seq=n_seq,
+                                capacity=cap, scale=float(1.0 / np.sqrt(128 + DK - DC)))
+        h = mla.mk_mla_create(cfg)
+        info = mla.mk_mla_get_info(h)
+        cache = torch.empty(n_seq, cap, DK, dtype=torch.bfloat16, device="cuda")
+        synth.device_normal(cache.data_ptr(), cache.numel(), synth.BF16, 9, synth.stream_id(-1, synth.K_MLA_CACHE))
+        q = torch.empty(rows, H, DK, dtype=torch.float32, device="cuda")
+        synth.device_normal(q.data_ptr(), q.numel(), synth.F32, 9, synth.stream_id(-1, synth.K_MLA_Q), 0.0, 0.25)
+        pos = torch.tensor([p0 + r % rps for r in range(rows)], dtype=torch.int32, device="cuda")
+        o = torch.empty(rows, H, DC, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        res = {}
+        for tag, fl in (("flushed", True), ("back_to_back", False)):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for t in range(warmup + steps):
+                if fl:
+                    flush[1].copy_(flush[0])
+                if t >= warmup:
+                    ev[t - warmup][0].record(stream)
+                mla.mk_mla_attention(h, q.data_ptr(), cache.data_ptr(), pos.data_ptr(), o.data_ptr(),
+                                     stream.cuda_stream)
+                if t >= warmup:
+                    ev[t - warmup][1].record(stream)
+            rc = mla.mk_mla_sync(h, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"{name}: mk_mla_sync returned {rc}")
+            res[tag] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        mla.mk_mla_destroy(h)
+        n_rows_read = (p0 + rps) * n_seq  # each sequence's rows 0 .. its last position, read once
+        byts = n_rows_read * DK * 2 + q.numel() * 4 + o.numel() * 4
+        ms = res["flushed"]
+        gbps = byts / (ms * 1e-3) / 1e9
+        r = dict(rows=rows, rows_per_seq=rps, sequences=n_seq, past_positions=p0, heads=H, splits=info.splits,
+                 workgroups=info.workgroups, launches=2, ms_per_call=ms, unflushed_ms_per_call=res["back_to_back"],
+                 bytes_per_call=float(byts), achieved_gbps=gbps, frac=gbps / PEAK_HBM_GBPS,
+                 finite=bool(torch.isfinite(o).all().item()))
+        log(f"{name}: {ms * 1e3:.1f} us per call flushed ({res['back_to_back'] * 1e3:.1f} back-to-back), "
+            f"{byts / 1e6:.1f} MB, {gbps:.0f} GB/s ({100 * r['frac']:.1f}% of peak), {info.workgroups} workgroups")
+        out[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        del cache, q, o
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_model():
     """The host CPU's model name (first processor of /proc/cpuinfo) and the
     number of processors the process may run on."""
@@ -389,6 +453,12 @@ def only_leg(torch, mk, args):
     from synth.stack import DeviceStack
     from synth.workloads import ATTN92_B8, MOE16_B8
     leg = args.only
+    if leg == "mla":
+        r = mla_legs(torch, args.steps, args.warmup)
+        if args.calib_copy_mib:
+            calib_copy(torch, args.calib_copy_mib)
+        print(json.dumps({"leg": leg, **r}), flush=True)
+        return
     if leg.startswith("moe16"):
         M = 1 if leg == "moe16_b1" else 8
         st = DeviceStack(MOE16_B8, n_layers=args.layers)
@@ -423,6 +493,7 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip the 8- and 64-row verify and speculative legs")
     ap.add_argument("--no-moe16", action="store_true", help="skip the 16-layer MoE-only legs")
     ap.add_argument("--no-phased", action="store_true", help="skip the one-launch-per-phase baseline legs")
+    ap.add_argument("--no-mla", action="store_true", help="skip the MLA attention legs")
     ap.add_argument("--moe16-steps", type=int, default=256, help="timed steps of the 16-layer legs")
     ap.add_argument("--cpu-layers", type=int, default=92, help="layers in the CPU-oracle sample (default: a whole step)")
     ap.add_argument("--cpu-layers-1t", type=int, default=12,
@@ -433,7 +504,7 @@ def main():
     ap.add_argument("--maps-out", default=None,
                     help="after the teardown, copy /proc/self/maps to this file (to name the owner of an address "
                          "in a crash report at exit)")
-    ap.add_argument("--only", choices=["batch1", "batch8", "verify8", "verify64", "moe16_b1", "moe16_b8"],
+    ap.add_argument("--only", choices=["batch1", "batch8", "verify8", "verify64", "moe16_b1", "moe16_b8", "mla"],
                     default=None, help="run only this leg (and --calib-copy-mib), print its record as JSON: the "
                                        "program of a counter pass")
     ap.add_argument("--pmc-kernel", default="1, 1>",
@@ -551,6 +622,9 @@ def main():
     moe16 = {}
     if not args.no_moe16:
         optional("moe16", lambda: moe16.update(moe16_legs(torch, mk, args.moe16_steps, args.warmup)))
+    mla_res = {}
+    if not args.no_mla:
+        optional("mla", lambda: mla_res.update(mla_legs(torch, min(args.steps, 20), args.warmup)))
     cpu = None
     if not args.no_cpu_baseline:
         def cpu_leg():
@@ -602,6 +676,7 @@ def main():
     out.update(verify)
     out.update(phased)
     out.update(moe16)
+    out.update(mla_res)
     if failed:
         out["failed_legs"] = failed
     print(json.dumps(out), flush=True)

@@ -20,12 +20,13 @@
  * and the head's output is W_UV,h out[r][h] (not done here).  Shapes follow
  * that model family: Dc = 512, Dr = 64.
  *
- * How.  One workgroup per (sequence, group of 16 query vectors, KV split):
- * cache tiles of 16 positions through LDS; scores on the matrix cores (each
- * wave a quarter of the 576 key columns, summed across the waves in a fixed
- * order), online softmax, and each wave the softmax-weighted sum over 128 of
- * the 512 latent columns on the matrix cores; then a second launch combines
- * the splits.  Queries enter the matrix cores as bf16 high and low parts
+ * How.  One workgroup per (sequence, group of 16 query vectors, KV split),
+ * two per CU: cache tiles of 32 positions through LDS, the next one in
+ * flight in registers; scores on the matrix cores (each wave a quarter of the
+ * 576 key columns, summed across the waves in a fixed order), online
+ * softmax, and each wave the softmax-weighted sum over 128 of the 512 latent
+ * columns on the matrix cores; then a second launch combines the splits
+ * (none with one split).  Queries enter the matrix cores as bf16 high and low parts
  * (about 16 significant bits), the cache as bf16 exactly, with fp32
  * accumulation.
  */

@@ -24,8 +24,7 @@ constexpr int kDc = 512;                         // latent columns (the values)
 constexpr int kDr = 64;                          // rotary key columns
 constexpr int kDk = kDc + kDr;                   // a cache row: the key
 constexpr int kRowBytes = kDk * 2;               // 1152 bytes of bf16
-constexpr int kTile = 16;                        // positions per tile
-constexpr int kTileU4 = kTile * kRowBytes / 16;  // 16-byte pieces of a tile (1152)
+constexpr int kTile = 32;                        // positions per tile: two halves of 16
 constexpr int kRowU4 = kRowBytes / 16;           // 72 per row
 // LDS row pitch: 1152 bytes is 288 dwords, which would put all 16 rows of a
 // matrix-core read on the same banks; 16 bytes of padding spread them.
@@ -37,7 +36,8 @@ constexpr int kChunks = kDk / 32;     // 18 key chunks of 32 columns
 constexpr int kMaxChunks = 5;         // waves take 5, 5, 4 and 4 chunks
 constexpr int kVals = kDc / kWaves;   // latent columns per wave (128)
 constexpr int kPartStride = 4 + kDc;  // floats per query of a split partial: m, l, -, -, acc[512]
-constexpr int kLoads = (kTileU4 + kThreads - 1) / kThreads;  // 16-byte loads per thread per tile (5)
+constexpr int kTileU4 = kTile * kRowBytes / 16;             // 16-byte pieces of a tile (2304)
+constexpr int kLoads = (kTileU4 + kThreads - 1) / kThreads;  // 16-byte loads per thread per tile (9)
 static_assert(kChunks == 2 * kMaxChunks + 2 * (kMaxChunks - 1), "chunk split");
 
 struct Params {
@@ -53,6 +53,7 @@ struct Params {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
@@ -61,9 +62,10 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
 }
 __device__ __forceinline__ short bf16_bits(__bf16 h) { return __builtin_bit_cast(short, h); }
 
-// A tile of 16 cache rows in flight through registers: piece u = thread +
+// A tile of 32 cache rows in flight through registers: piece u = thread +
 // 256k of the tile (row u / 72, 16 bytes at u % 72).  Rows past the capacity
-// re-read the last row (their scores are masked).
+// re-read the last row (their scores are masked).  (A native vector type:
+// an array of HIP's uint4 structs would be kept in scratch memory.)
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 struct Prefetch {
   u32x4_t v[kLoads];
@@ -87,10 +89,11 @@ __device__ __forceinline__ void store_tile(const Prefetch& pf, char* tile) {
 // Workgroup (seq, qg, s): the 16 query vectors qg*16 .. qg*16+15 of sequence
 // seq (query i of a sequence is row i / H, head i % H; H is a multiple of
 // 16, so the 16 share one row and one position) against split s of the
-// row's positions, tiles of 16 positions.
+// row's positions, tiles of 32 positions.  With one split the workgroup
+// writes the outputs itself (no combine launch).
 __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char tile[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) f32x4_t exch[kWaves][64];
+  __shared__ __attribute__((aligned(16))) f32x4_t exch[2][kWaves][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int s = blockIdx.x % p.S, qg = (blockIdx.x / p.S) % p.QG, seq = blockIdx.x / (p.S * p.QG);
   const int row = seq * p.rps + (qg * kQ) / p.H;
@@ -124,11 +127,11 @@ __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
       }
     }
   }
-  Prefetch pf;
   f32x4_t acc[kVals / 16];
 #pragma unroll
   for (int nb = 0; nb < kVals / 16; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_l = -INFINITY, lsum = 0.f;
+  Prefetch pf;
   if (t_lo < t_hi) {
     load_tile(pf, rows, t_lo, p.cap);
     store_tile(pf, tile);
@@ -137,40 +140,53 @@ __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
   for (int t = t_lo; t < t_hi; ++t) {
     // the next tile (at the last one, this one again) lands while this one is used
     load_tile(pf, rows, min(t + 1, t_hi - 1), p.cap);
-    // partial scores over this wave's chunks: D lane l = positions 4(l>>4)+i, query l&15
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    // partial scores over this wave's chunks for both halves of the tile:
+    // D lane l = positions 4(l>>4)+i of the half, query l&15
+    f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
     {
       const char* kr = tile + qq * kPitch + lg * 16;
 #pragma unroll
       for (int c = 0; c < kMaxChunks; ++c) {
         if (c < nc) {
-          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kr + (c0 + c) * 64));
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[c], sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[c], sc, 0, 0, 0);
+          const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kr + (c0 + c) * 64));
+          const bf16x8_t kb =
+              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kr + 16 * kPitch + (c0 + c) * 64));
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[c], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qh[c], sb, 0, 0, 0);
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[c], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, ql[c], sb, 0, 0, 0);
         }
       }
     }
-    exch[wave][lane] = sc;
+    exch[0][wave][lane] = sa;
+    exch[1][wave][lane] = sb;
     __syncthreads();
     // full scores: the four waves' partials in a fixed order (every wave
-    // then holds the same values)
-    float sv[4];
+    // then holds the same values); sv[0..3] first half, sv[4..7] second
+    float sv[8];
     {
-      f32x4_t tot = exch[0][lane];
+      f32x4_t ta = exch[0][0][lane], tb = exch[1][0][lane];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) tot += exch[w][lane];
+      for (int w = 1; w < kWaves; ++w) {
+        ta += exch[0][w][lane];
+        tb += exch[1][w][lane];
+      }
       bool up = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int jpos = t * kTile + 4 * lg + i;
-        sv[i] = jpos < npos ? tot[i] : -INFINITY;
-        up |= sv[i] > m_l + 8.f;
+        const int ja = t * kTile + 4 * lg + i;
+        sv[i] = ja < npos ? ta[i] : -INFINITY;
+        sv[4 + i] = ja + 16 < npos ? tb[i] : -INFINITY;
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) up |= sv[i] > m_l + 8.f;
       // online softmax in base 2 with a reference maximum that is raised
       // only when a score exceeds it by more than 8 (2^8 stays exact enough
       // in fp32); wave-uniform
       if (__builtin_amdgcn_ballot_w64(up) != 0) {
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        float mx = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const bool raise = mx > m_l + 8.f;
@@ -181,34 +197,50 @@ __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
         m_l = raise ? mx : m_l;
       }
     }
-    s16x4_t ph, pl;
+    // The weights as the B operand of a 32-deep product, lane l: query l&15,
+    // k-slots 8(l>>4) .. +7 = positions 4(l>>4) .. +3 of the first half and
+    // of the second half (the score layouts as they are); the V^T operand
+    // below uses the same k-slot order.
+    s16x8_t ph, pl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const float pv = sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_l);
       lsum += pv;
       const __bf16 h = (__bf16)pv;
       ph[i] = bf16_bits(h);
       pl[i] = bf16_bits((__bf16)(pv - (float)h));
     }
-    // this wave's 128 latent columns: V^T operand by transpose loads, lane
-    // 16g + 4j + c reads position 4g + j, columns 128w + 16nb + 4c .. +3
+    // this wave's 128 latent columns: V^T by transpose loads, lane 16g + 4j
+    // + c reads position 4g + j of each half, columns 128w + 16nb + 4c .. +3
     {
       const char* vr = tile + (4 * lg + ((lane >> 2) & 3)) * kPitch + wave * kVals * 2 + (lane & 3) * 8;
+      const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, ph), bl = __builtin_bit_cast(bf16x8_t, pl);
 #pragma unroll
       for (int nb = 0; nb < kVals / 16; ++nb) {
-        const s16x4_t vt = lds_read_tr16(vr + nb * 32);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, acc[nb], 0, 0, 0);
+        const s16x4_t va = lds_read_tr16(vr + nb * 32);
+        const s16x4_t vb = lds_read_tr16(vr + 16 * kPitch + nb * 32);
+        const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, bh, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, bl, acc[nb], 0, 0, 0);
       }
     }
     __syncthreads();  // every wave is done with the tile and the exchange slots
     store_tile(pf, tile);
     __syncthreads();
   }
-  // the split's partial: m (natural units), l, and the sums, query-major
   float lw = lsum;
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
+  if (p.S == 1) {  // the whole range: the outputs themselves (zero for a rejected row)
+    const float inv = lw > 0.f ? 1.f / lw : 0.f;
+    float* o = p.out + ((size_t)row * p.H + (qg * kQ) % p.H + qq) * kDc + wave * kVals + 4 * lg;
+#pragma unroll
+    for (int nb = 0; nb < kVals / 16; ++nb)
+      *reinterpret_cast<float4*>(o + nb * 16) =
+          make_float4(acc[nb][0] * inv, acc[nb][1] * inv, acc[nb][2] * inv, acc[nb][3] * inv);
+    return;
+  }
+  // the split's partial: m (natural units), l, and the sums, query-major
   constexpr float kLn2 = 0.6931471805599453f;
   float* dst = p.part + ((size_t)((seq * p.QG + qg) * p.S + s) * kQ + qq) * kPartStride;
 #pragma unroll
@@ -230,10 +262,12 @@ __global__ void __launch_bounds__(128) combine_kernel(Params p) {
   const float* base = p.part + ((size_t)((seq * p.QG + qg) * p.S) * kQ + q) * kPartStride;
   const size_t sstride = (size_t)kQ * kPartStride;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < p.S; ++s) M = fmaxf(M, base[s * sstride]);
   float L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   const int d = threadIdx.x * 4;
+#pragma unroll 8
   for (int s = 0; s < p.S; ++s) {
     const float* b = base + s * sstride;
     const float w = b[0] == -INFINITY ? 0.f : __expf(b[0] - M);
@@ -303,11 +337,13 @@ int mk_mla_create(const mk_mla_config* cfg, mk_mla_handle** out) {
   h->device = dev;
   h->n_seq_step = c.rows / c.rows_per_seq;
   h->QG = c.n_heads * c.rows_per_seq / kQ;
-  // splits: about two workgroups per CU, each with at least one tile
+  // splits: about two workgroups per CU (two tiles in flight per CU), each
+  // with at least 4 tiles of the full capacity (a split's partial, 33 KB,
+  // should stay well below the 147 KB of cache rows it reads)
   const int base = h->n_seq_step * h->QG;
-  const int want = (2 * prop.multiProcessorCount + base - 1) / base;
-  const int tiles = (c.capacity + kTile - 1) / kTile;
-  h->S = want < 1 ? 1 : (want > tiles ? tiles : want);
+  const int want = (2 * prop.multiProcessorCount + base / 2) / base;
+  const int most = (c.capacity + 4 * kTile - 1) / (4 * kTile);
+  h->S = want < 1 ? 1 : (want > most ? most : want);
   h->part_bytes = (size_t)base * h->S * kQ * kPartStride * sizeof(float);
   if (hipMalloc(&h->part, h->part_bytes) != hipSuccess) {
     delete h;
@@ -348,6 +384,7 @@ int mk_mla_attention(mk_mla_handle* h, const float* q, const uint16_t* cache, co
   hipLaunchKernelGGL(split_kernel, dim3(h->n_seq_step * h->QG * h->S), dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MK_ERR_HIP, "split launch failed: %s", hipGetErrorString(e));
+  if (h->S == 1) return MK_OK;  // the split launch wrote the outputs
   hipLaunchKernelGGL(combine_kernel, dim3(c.rows * c.n_heads), dim3(128), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(MK_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
