@@ -123,9 +123,13 @@ def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush
     if rc != mk.MK_OK:
         raise mk.MkError(rc, mk.mk_last_error())
     durs = np.array([a.elapsed_time(b) for a, b in ev])  # ms, per launch
+    tasks = None
     if trace_union:
         idn = ids.cpu().numpy()
         unions = [[len(np.unique(idn[t, l])) for l in range(st.L)] for t in range(total)]
+        if M > 8:  # row groups in one launch: routed tasks of at most 8 rows per expert
+            tasks = float(np.mean([sum(-(-int(c) // 8) for c in np.bincount(idn[t, l].ravel(), minlength=w.E))
+                                   for t in range(warmup, total) for l in range(st.L)]))
     else:
         unions = [[w.k] * st.L for _ in range(total)]
     byts = [step_bytes(w, M, n_seq, unions[t], 0) + st.L * n_seq * (int(pos[t].max()) + 1) * 2 * w.G * w.hd * 2
@@ -143,7 +147,8 @@ def run_leg(torch, mk, st, w, M, rows_per_seq, steps, warmup, trace_union, flush
                 wall_ms_per_step=t_wall * 1e3 / steps, tok_s=M / (ms * 1e-3), bytes_per_step=float(np.mean(byts)),
                 achieved_gbps=gbps, frac=gbps / PEAK_HBM_GBPS,
                 union_mean=float(np.mean([np.mean(u) for u in unions[warmup:]])), barriers=info.barriers_per_step,
-                finite=finite, union_per_layer=union_layers if trace_union else None, launches=launches)
+                finite=finite, union_per_layer=union_layers if trace_union else None, launches=launches,
+                **({"tasks_per_layer": tasks} if tasks is not None else {}))
 
 
 def spec_leg(torch, mk, st, w, n_seq, steps, warmup, alpha=0.9155, seed=5):
