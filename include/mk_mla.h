@@ -48,7 +48,7 @@ typedef struct mk_mla_config {
   int32_t rows;         /* M: rows per call, 1..64, fixed per handle */
   int32_t rows_per_seq; /* rows of one sequence (1 at decode; 8 for a verify pass); divides rows */
   int32_t n_seq;        /* sequences in the cache, >= rows / rows_per_seq */
-  int32_t capacity;     /* positions per sequence in the cache, >= 1 */
+  int32_t capacity;     /* positions per sequence in the cache, 1 .. 2^21 */
   float scale;          /* softmax scale, > 0 (1/sqrt(d_nope + Dr) in the published model) */
 } mk_mla_config;
 

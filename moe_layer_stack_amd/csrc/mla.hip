@@ -63,27 +63,44 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
 __device__ __forceinline__ short bf16_bits(__bf16 h) { return __builtin_bit_cast(short, h); }
 
 // A tile of 32 cache rows in flight through registers: piece u = thread +
-// 256k of the tile (row u / 72, 16 bytes at u % 72).  Rows past the capacity
-// re-read the last row (their scores are masked).  (A native vector type:
-// an array of HIP's uint4 structs would be kept in scratch memory.)
+// 256k of the tile (row u / 72, 16 bytes at u % 72); 2304 pieces, 9 per
+// thread exactly.  A thread's pieces sit at the same place in every tile, so
+// their rows and offsets are worked out once (TileMap) and a tile costs one
+// row clamp and one 32-bit offset per piece.  Rows past the capacity re-read
+// the last row (their scores are masked).  (A native vector type: an array
+// of HIP's uint4 structs would be kept in scratch memory.)
+static_assert(kTileU4 == kLoads * kThreads, "every thread moves the same number of pieces");
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 struct Prefetch {
   u32x4_t v[kLoads];
 };
-__device__ __forceinline__ void load_tile(Prefetch& pf, const uint16_t* rows, int t, int cap) {
-#pragma unroll
-  for (int k = 0; k < kLoads; ++k) {
-    const int u = min((int)threadIdx.x + k * kThreads, kTileU4 - 1);
-    const int r = min(t * kTile + u / kRowU4, cap - 1);
-    pf.v[k] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(rows + (size_t)r * kDk) + (u % kRowU4) * 16);
-  }
-}
-__device__ __forceinline__ void store_tile(const Prefetch& pf, char* tile) {
+struct TileMap {
+  int row[kLoads];  // row of the piece within the tile
+  int off[kLoads];  // byte offset of the piece within its row
+};
+__device__ __forceinline__ TileMap tile_map() {
+  TileMap m;
 #pragma unroll
   for (int k = 0; k < kLoads; ++k) {
     const int u = (int)threadIdx.x + k * kThreads;
-    if (u < kTileU4) *reinterpret_cast<u32x4_t*>(tile + (u / kRowU4) * kPitch + (u % kRowU4) * 16) = pf.v[k];
+    m.row[k] = u / kRowU4;
+    m.off[k] = (u % kRowU4) * 16;
   }
+  return m;
+}
+// rows: the sequence's cache (its first row); offsets stay below 2^32 for
+// capacities below 3.7 million positions (the host checks)
+__device__ __forceinline__ void load_tile(Prefetch& pf, const char* rows, const TileMap& m, int t, int cap) {
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) {
+    const unsigned r = (unsigned)min(t * kTile + m.row[k], cap - 1);
+    pf.v[k] = *reinterpret_cast<const u32x4_t*>(rows + (r * (unsigned)kRowBytes + (unsigned)m.off[k]));
+  }
+}
+__device__ __forceinline__ void store_tile(const Prefetch& pf, char* tile, const TileMap& m) {
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k)
+    *reinterpret_cast<u32x4_t*>(tile + m.row[k] * kPitch + m.off[k]) = pf.v[k];
 }
 
 // Workgroup (seq, qg, s): the 16 query vectors qg*16 .. qg*16+15 of sequence
@@ -103,7 +120,7 @@ __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
   const int npos = ok ? pos + 1 : 0;
   const int ntile = (npos + kTile - 1) / kTile;
   const int t_lo = (int)(((long long)s * ntile) / p.S), t_hi = (int)(((long long)(s + 1) * ntile) / p.S);
-  const uint16_t* rows = p.cache + (size_t)seq * p.cap * kDk;
+  const char* rows = reinterpret_cast<const char*>(p.cache + (size_t)seq * p.cap * kDk);
   const int qq = lane & 15, lg = lane >> 4;
   // This wave's key chunks and its query operand for them, lane l: query
   // l & 15, columns 32c + 8(l >> 4) .. +7, bf16 high and low parts.
@@ -132,14 +149,15 @@ __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
   for (int nb = 0; nb < kVals / 16; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_l = -INFINITY, lsum = 0.f;
   Prefetch pf;
+  const TileMap tm = tile_map();
   if (t_lo < t_hi) {
-    load_tile(pf, rows, t_lo, p.cap);
-    store_tile(pf, tile);
+    load_tile(pf, rows, tm, t_lo, p.cap);
+    store_tile(pf, tile, tm);
   }
   __syncthreads();
   for (int t = t_lo; t < t_hi; ++t) {
     // the next tile (at the last one, this one again) lands while this one is used
-    load_tile(pf, rows, min(t + 1, t_hi - 1), p.cap);
+    load_tile(pf, rows, tm, min(t + 1, t_hi - 1), p.cap);
     // partial scores over this wave's chunks for both halves of the tile:
     // D lane l = positions 4(l>>4)+i of the half, query l&15
     f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -225,7 +243,7 @@ __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
       }
     }
     __syncthreads();  // every wave is done with the tile and the exchange slots
-    store_tile(pf, tile);
+    store_tile(pf, tile, tm);
     __syncthreads();
   }
   float lw = lsum;
@@ -322,9 +340,9 @@ int mk_mla_create(const mk_mla_config* cfg, mk_mla_handle** out) {
   if (c.latent_dim != kDc || c.rope_dim != kDr)
     return fail(MK_ERR_UNSUPPORTED, "latent_dim %d / rope_dim %d: the kernel is built for %d / %d", c.latent_dim,
                 c.rope_dim, kDc, kDr);
-  if (c.n_heads % kQ != 0 || c.n_heads > 128 || c.rows > 64)
-    return fail(MK_ERR_UNSUPPORTED, "n_heads %d (16, 32, 64 or 128) or rows %d (<= 64) out of range", c.n_heads,
-                c.rows);
+  if (c.n_heads % kQ != 0 || c.n_heads > 128 || c.rows > 64 || c.capacity > (1 << 21))
+    return fail(MK_ERR_UNSUPPORTED, "n_heads %d (16, 32, 64 or 128), rows %d (<= 64) or capacity %d (<= 2^21) out of range",
+                c.n_heads, c.rows, c.capacity);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MK_ERR_DEVICE, "no HIP device");
   hipDeviceProp_t prop;

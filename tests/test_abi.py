@@ -58,7 +58,8 @@ def test_mla_create_rejects_bad_configs_before_the_device(mk):
                       (dict(n_seq=4), mk.MK_ERR_INVALID_ARG), (dict(scale=0.0), mk.MK_ERR_INVALID_ARG),
                       (dict(scale=float("nan")), mk.MK_ERR_INVALID_ARG), (dict(latent_dim=256), mk.MK_ERR_UNSUPPORTED),
                       (dict(rope_dim=32), mk.MK_ERR_UNSUPPORTED), (dict(n_heads=8), mk.MK_ERR_UNSUPPORTED),
-                      (dict(n_heads=256), mk.MK_ERR_UNSUPPORTED), (dict(rows=72, n_seq=72), mk.MK_ERR_UNSUPPORTED)):
+                      (dict(n_heads=256), mk.MK_ERR_UNSUPPORTED), (dict(rows=72, n_seq=72), mk.MK_ERR_UNSUPPORTED),
+                      (dict(capacity=(1 << 21) + 1), mk.MK_ERR_UNSUPPORTED)):
         cfg = mla.mk_mla_config(**{**good, **bad})
         assert L.mk_mla_create(C.byref(cfg), C.byref(h)) == want, bad
         assert h.value is None

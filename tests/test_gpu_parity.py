@@ -79,6 +79,34 @@ def test_verify_prefix_m8(env):
     _run_and_check(env, VERIFY92_M8, n_layers=2)
 
 
+@pytest.mark.parametrize("M", [16, 32])
+def test_row_groups_in_one_launch_moe16(env, M):
+    """2 and 4 row groups of 8 independent rows in one launch on the MoE-only
+    stack (no attention: the routed tasks read each row's layer input, the
+    step input at layer 0 and the previous layer's output after it), 3
+    layers, against the oracle."""
+    import moe_layer_stack_amd as mk
+    from synth.stack import DeviceStack
+    from synth.workloads import MOE16_B8
+    w = MOE16_B8.with_(name=f"moe16_rows{M}", M=M)
+    st = DeviceStack(w, n_layers=3)
+    h = mk.mk_create(st.config(), st.layer_weights())
+    try:
+        assert mk.mk_get_info(h).launches_per_step == 1
+    finally:
+        mk.mk_destroy(h)
+    del st
+    _run_and_check(env, w, n_layers=3)
+
+
+@pytest.mark.parametrize("M", [16, 32])
+def test_row_groups_in_one_launch_verify(env, M):
+    """2 and 4 sequences x 8 verify rows in one launch (row groups with
+    routed tasks), 2-layer prefix of the 92-layer stack, against the oracle."""
+    from synth.workloads import VERIFY92_M64
+    _run_and_check(env, VERIFY92_M64.with_(name=f"verify92_m{M}", M=M), n_layers=2)
+
+
 def test_device_generator_matches_host(env):
     import synth
     torch = env
