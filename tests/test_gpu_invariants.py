@@ -386,80 +386,112 @@ def test_moe16_feedback_steps(env):
         run.close()
 
 
-@pytest.mark.timeout(1500)
-def test_attn92_full_depth_batch1_batch8_verify8_and_verify64(env):
-    """The benchmark's stack at full depth (92 layers), every step against the
-    oracle walked over the same bytes: batch 1 (sequence 0), batch 8 (all 8
-    rows, each its own sequence), a verify pass of 8 rows of sequence 0, and
-    a verify pass of 8 rows of each of the 8 sequences in one launch, whose
-    sequence 5 is walked (its routed work ran in tasks mixed with the other
-    sequences' rows).  Every checked step's output, expert sets, routing
-    weights and all the K/V rows it appended (92 layers x rows x 8 kv heads)
-    are checked; batch-8 row 0 also equals the batch-1 step."""
-    import moe_layer_stack_amd as mk
-    from parity_util import (GpuRun, assert_close, assert_kv_rows, assert_routing_weights, oracle_walk,
-                             tolerances)
+# The benchmark's stack at full depth (92 layers), every step against the
+# oracle walked over the same bytes, in four tests over one stack (each
+# takes the cache as it stands right before its own step): batch 1 (sequence
+# 0); batch 8 (all 8 rows, each its own sequence); a verify pass of 8 rows
+# of sequence 0; and a verify pass of 8 rows of each of the 8 sequences in
+# one launch, whose sequence 5 is walked (its routed work ran in tasks mixed
+# with the other sequences' rows).  Every checked step's output, expert sets,
+# routing weights and all the K/V rows it appended (92 layers x rows x 8 kv
+# heads) are checked.
+
+
+@pytest.fixture(scope="module")
+def stack92(env):
     from synth.workloads import ATTN92_B8
     torch = env
-    w8 = ATTN92_B8
-    tol = tolerances(w8)
-    _say(f"full depth {w8.name} L={w8.L}")
-    st = _stack(w8)
+    _say(f"full depth {ATTN92_B8.name}: building L={ATTN92_B8.L}")
+    st = _stack(ATTN92_B8)
+    yield st
+    del st
+    torch.cuda.empty_cache()
 
-    def walk(tag, hid, pos, ids, rps, kv_hosts):
-        def progress(l):
-            if l % 23 == 0:
-                _say(f"full depth {tag}: oracle at layer {l}")
-        return oracle_walk(st, hid, pos, ids, rows_per_seq=rps, kv_hosts=kv_hosts, progress=progress)
 
-    def check(tag, out, hid, pos, run, rps, kv_hosts, rows=None, seq0=0):
-        ids, wts, logits = run.trace()
-        if rows is not None:  # a slice of the step's rows (whole sequences)
-            ids, wts, logits = ids[:, rows], wts[:, rows], logits[:, rows]
-        M = ids.shape[1]
-        ref, rep = walk(tag, hid, pos, ids, rps, kv_hosts)
-        assert not rep["mismatch"], (tag, rep["mismatch"][:3])
-        c = assert_close(out.cpu().numpy(), ref, tol, f"full depth {tag}")
-        assert_routing_weights(ids, wts, logits, rep, M, st.L, what=tag)
-        c.update(assert_kv_rows(st, rep, pos, rps, what=f"full depth {tag}", seq0=seq0))
-        _say(f"full depth {tag} {c} forced={rep['forced']}")
+def _full_depth_check(st, tag, out, hid, pos, run, rps, kv_hosts, rows=None, seq0=0):
+    from parity_util import assert_close, assert_kv_rows, assert_routing_weights, oracle_walk, tolerances
+    ids, wts, logits = run.trace()
+    if rows is not None:  # a slice of the step's rows (whole sequences)
+        ids, wts, logits = ids[:, rows], wts[:, rows], logits[:, rows]
+    M = ids.shape[1]
 
+    def progress(l):
+        if l % 23 == 0:
+            _say(f"full depth {tag}: oracle at layer {l}")
+    ref, rep = oracle_walk(st, hid, pos, ids, rows_per_seq=rps, kv_hosts=kv_hosts, progress=progress)
+    assert not rep["mismatch"], (tag, rep["mismatch"][:3])
+    c = assert_close(out.cpu().numpy(), ref, tolerances(st.w), f"full depth {tag}")
+    assert_routing_weights(ids, wts, logits, rep, M, st.L, what=tag)
+    c.update(assert_kv_rows(st, rep, pos, rps, what=f"full depth {tag}", seq0=seq0))
+    _say(f"full depth {tag} {c} forced={rep['forced']}")
+
+
+@pytest.mark.timeout(900)
+def test_attn92_full_depth_batch1(env, stack92):
+    """Batch 1 on sequence 0."""
+    from parity_util import GpuRun
+    st = stack92
     hid = st.hidden(0)
-    pos = w8.positions(0)
-    # batch 1: sequence 0
+    pos = st.w.positions(0)
     kv0 = [tuple(x[:1].copy() for x in st.host_kv(l)) for l in range(st.L)]
     r1 = GpuRun(st, rows=1, rows_per_seq=1)
     try:
         o1 = r1.step(hid[:1].contiguous(), pos[:1]).clone()
-        check("batch 1", o1, hid[:1].cpu().numpy(), pos[:1], r1, 1, kv0)
+        _full_depth_check(st, "batch 1", o1, hid[:1].cpu().numpy(), pos[:1], r1, 1, kv0)
     finally:
         r1.close()
-    del kv0
-    # batch 8: 8 sequences, one row each, over the cache as it stands now
+
+
+@pytest.mark.timeout(900)
+def test_attn92_full_depth_batch8(env, stack92):
+    """Batch 8 on all 8 sequences (one row each); its row 0 also equals a
+    batch-1 step of sequence 0 at the same position, taken just before."""
+    from parity_util import GpuRun, assert_close, tolerances
+    st = stack92
+    hid = st.hidden(0)
+    pos = st.w.positions(0)
+    r1 = GpuRun(st, rows=1, rows_per_seq=1)
+    try:
+        o1 = r1.step(hid[:1].contiguous(), pos[:1]).cpu().numpy()
+    finally:
+        r1.close()
+    # the batch-1 step wrote sequence 0's row at pos[0]; batch 8 rewrites it
     kv8 = [st.host_kv(l) for l in range(st.L)]
     r8 = GpuRun(st)
     try:
         o8 = r8.step(hid, pos).clone()
-        check("batch 8", o8, hid.cpu().numpy(), pos, r8, 1, kv8)
+        _full_depth_check(st, "batch 8", o8, hid.cpu().numpy(), pos, r8, 1, kv8)
     finally:
         r8.close()
-    del kv8
-    assert_close(o8[:1].cpu().numpy(), o1.cpu().numpy(), tol, "full depth batch-8 row 0")
-    # verify: 8 rows of sequence 0 at positions past .. past+7 (the first of
-    # them overwrites the batch steps' row), causal among the drafts
-    pv = [w8.past + r for r in range(8)]
+    assert_close(o8[:1].cpu().numpy(), o1, tolerances(st.w), "full depth batch-8 row 0")
+
+
+@pytest.mark.timeout(900)
+def test_attn92_full_depth_verify8(env, stack92):
+    """8 rows of sequence 0 at positions past .. past+7, causal among the
+    drafts (the first of them overwrites the batch steps' row)."""
+    from parity_util import GpuRun
+    st = stack92
+    pv = [st.w.past + r for r in range(8)]
     kvv = [tuple(x[:1].copy() for x in st.host_kv(l)) for l in range(st.L)]
     rv = GpuRun(st, rows=8, rows_per_seq=8)
     try:
         hv = st.hidden(1)
         ov = rv.step(hv, pv).clone()
-        check("verify 1 x 8", ov, hv.cpu().numpy(), pv, rv, 8, kvv)
+        _full_depth_check(st, "verify 1 x 8", ov, hv.cpu().numpy(), pv, rv, 8, kvv)
     finally:
         rv.close()
-    del kvv
-    # verify: 8 rows of each of the 8 sequences in one launch; sequence 5
+
+
+@pytest.mark.timeout(900)
+def test_attn92_full_depth_verify64(env, stack92):
+    """8 rows of each of the 8 sequences in one launch; sequence 5 walked."""
+    import moe_layer_stack_amd as mk
+    from parity_util import GpuRun
+    torch = env
+    st = stack92
     s5 = 5
-    p64 = [w8.past + r for _ in range(8) for r in range(8)]
+    p64 = [st.w.past + r for _ in range(8) for r in range(8)]
     kv5 = [tuple(x[s5:s5 + 1].copy() for x in st.host_kv(l)) for l in range(st.L)]
     r64 = GpuRun(st, rows=64, rows_per_seq=8)
     try:
@@ -467,8 +499,8 @@ def test_attn92_full_depth_batch1_batch8_verify8_and_verify64(env):
         h64 = st.hidden(2, rows=64)
         o64 = r64.step(h64, p64).clone()
         rows5 = slice(8 * s5, 8 * s5 + 8)
-        check("verify 8 x 8, sequence 5", o64[rows5], h64[rows5].cpu().numpy(), p64[rows5], r64, 8, kv5,
-              rows=rows5, seq0=s5)
+        _full_depth_check(st, "verify 8 x 8, sequence 5", o64[rows5], h64[rows5].cpu().numpy(), p64[rows5], r64, 8,
+                          kv5, rows=rows5, seq0=s5)
         assert torch.isfinite(o64).all()
     finally:
         r64.close()
