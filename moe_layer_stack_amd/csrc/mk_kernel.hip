@@ -1462,39 +1462,59 @@ __device__ __forceinline__ void attn_prologue(const KParams& p, const Misc* ms, 
   const int nrows_qkv = (p.H + 2 * p.G) * hd;
   const float* qkv = act_f(p, l, p.al.qkv);
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int it = threadIdx.x; it < Q * (hd / 2); it += kThreads) {
-    const int q = it / (hd / 2), i = it % (hd / 2);
-    const int qa = qbase + q;  // query index within the (sequence, kv head)
-    const int row = seq * rps + qa / HG, head = g * HG + qa % HG;
-    const float* src = qkv + (size_t)row * nrows_qkv + head * hd;
-    const float c = ms->rope[(row * 64 + i) * 2], sn = ms->rope[(row * 64 + i) * 2 + 1];
-    const float x0 = src[i], x1 = src[i + hd / 2];
-    Qv[q * hd + i] = (x0 * c - x1 * sn) * scale;
-    Qv[q * hd + i + hd / 2] = (x1 * c + x0 * sn) * scale;
-  }
   uint16_t* kc = reinterpret_cast<uint16_t*>(const_cast<char*>(P.b0));
   uint16_t* vc = reinterpret_cast<uint16_t*>(const_cast<char*>(P.b1));
-  for (int it = threadIdx.x; it < rps * (hd / 2); it += kThreads) {
-    const int rr = it / (hd / 2), i = it % (hd / 2);
-    const int row = seq * rps + rr;
-    const int pos = ms->pos[row];
-    if (pos < p_lo || pos >= p_hi) continue;
-    const float* ksrc = qkv + (size_t)row * nrows_qkv + p.H * hd + g * hd;
-    const float* vsrc = qkv + (size_t)row * nrows_qkv + (p.H + p.G) * hd + g * hd;
-    const float c = ms->rope[(row * 64 + i) * 2], sn = ms->rope[(row * 64 + i) * 2 + 1];
-    const float x0 = ksrc[i], x1 = ksrc[i + hd / 2];
-    const uint16_t k0 = f32_to_bf16(x0 * c - x1 * sn), k1 = f32_to_bf16(x1 * c + x0 * sn);
-    const uint16_t v0 = f32_to_bf16(vsrc[i]), v1 = f32_to_bf16(vsrc[i + hd / 2]);
-    if (write_cache) {  // one query group of the (sequence, kv head) writes the cache
-      kc[(size_t)pos * hd + i] = k0;
-      kc[(size_t)pos * hd + i + hd / 2] = k1;
-      vc[(size_t)pos * hd + i] = v0;
-      vc[(size_t)pos * hd + i + hd / 2] = v1;
+  // One pass over the query items and the new-row items (item it covers
+  // element pair i, i + hd/2 of both kinds): every global read of an item is
+  // issued before its arithmetic, so the split that owns this step's row
+  // reads its k, v in the same round trip as the queries.
+  const int nq_it = Q * (hd / 2), nk_it = rps * (hd / 2);
+  const int n_it = nq_it > nk_it ? nq_it : nk_it;
+  for (int it = threadIdx.x; it < n_it; it += kThreads) {
+    const int i = it % (hd / 2);
+    const bool dq = it < nq_it;
+    const int q = it / (hd / 2);
+    const int qa = qbase + q;  // query index within the (sequence, kv head)
+    const int qrow = seq * rps + qa / HG, head = g * HG + qa % HG;
+    float x0 = 0.f, x1 = 0.f;
+    if (dq) {
+      const float* src = qkv + (size_t)qrow * nrows_qkv + head * hd;
+      x0 = src[i];
+      x1 = src[i + hd / 2];
     }
-    nkb[rr * 128 + i] = k0;
-    nkb[rr * 128 + i + hd / 2] = k1;
-    nvb[rr * 128 + i] = v0;
-    nvb[rr * 128 + i + hd / 2] = v1;
+    const int rr = it / (hd / 2);
+    const int krow = seq * rps + rr;
+    const int pos = it < nk_it ? ms->pos[krow] : -1;
+    const bool dk = it < nk_it && pos >= p_lo && pos < p_hi;
+    float y0 = 0.f, y1 = 0.f, u0 = 0.f, u1 = 0.f;
+    if (dk) {
+      const float* ksrc = qkv + (size_t)krow * nrows_qkv + p.H * hd + g * hd;
+      const float* vsrc = qkv + (size_t)krow * nrows_qkv + (p.H + p.G) * hd + g * hd;
+      y0 = ksrc[i];
+      y1 = ksrc[i + hd / 2];
+      u0 = vsrc[i];
+      u1 = vsrc[i + hd / 2];
+    }
+    if (dq) {
+      const float c = ms->rope[(qrow * 64 + i) * 2], sn = ms->rope[(qrow * 64 + i) * 2 + 1];
+      Qv[q * hd + i] = (x0 * c - x1 * sn) * scale;
+      Qv[q * hd + i + hd / 2] = (x1 * c + x0 * sn) * scale;
+    }
+    if (dk) {
+      const float c = ms->rope[(krow * 64 + i) * 2], sn = ms->rope[(krow * 64 + i) * 2 + 1];
+      const uint16_t k0 = f32_to_bf16(y0 * c - y1 * sn), k1 = f32_to_bf16(y1 * c + y0 * sn);
+      const uint16_t v0 = f32_to_bf16(u0), v1 = f32_to_bf16(u1);
+      if (write_cache) {  // one query group of the (sequence, kv head) writes the cache
+        kc[(size_t)pos * hd + i] = k0;
+        kc[(size_t)pos * hd + i + hd / 2] = k1;
+        vc[(size_t)pos * hd + i] = v0;
+        vc[(size_t)pos * hd + i + hd / 2] = v1;
+      }
+      nkb[rr * 128 + i] = k0;
+      nkb[rr * 128 + i + hd / 2] = k1;
+      nvb[rr * 128 + i] = v0;
+      nvb[rr * 128 + i + hd / 2] = v1;
+    }
   }
 }
 
