@@ -20,15 +20,16 @@
  * and the head's output is W_UV,h out[r][h] (not done here).  Shapes follow
  * that model family: Dc = 512, Dr = 64.
  *
- * How.  One workgroup per (sequence, group of 16 query vectors, KV split),
- * two per CU: cache tiles of 32 positions through LDS, the next one in
- * flight in registers; scores on the matrix cores (each wave a quarter of the
- * 576 key columns, summed across the waves in a fixed order), online
- * softmax, and each wave the softmax-weighted sum over 128 of the 512 latent
- * columns on the matrix cores; then a second launch combines the splits
- * (none with one split).  Queries enter the matrix cores as bf16 high and low parts
- * (about 16 significant bits), the cache as bf16 exactly, with fp32
- * accumulation.
+ * How.  Cache tiles of 32 positions through LDS, scores and the weighted
+ * sum on the matrix cores, online softmax, the positions split over
+ * workgroups whose partials a second launch combines (none with one split).
+ * A sequence with few query vectors (decode: the H heads of one row) takes
+ * workgroups of 16 vectors, two per CU, the 576 key columns split over the 4
+ * waves and summed in a fixed order; a sequence with 128 or more (verify
+ * blocks of several rows) takes workgroups of 64 vectors (8 waves, one per
+ * CU), so that every tile is read once for 64 vectors.  Queries enter the
+ * matrix cores as bf16 high and low parts (about 16 significant bits), the
+ * cache as bf16 exactly, with fp32 accumulation.
  */
 #ifndef MK_MLA_H
 #define MK_MLA_H
