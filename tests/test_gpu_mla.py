@@ -172,3 +172,25 @@ def test_mla_rejected_position(env):
         assert rc == mk.MK_ERR_INVALID_ARG
         assert (o[1] == 0).all()
         _check(o, q, cache, pos, 1, SCALE, "row 0 beside a rejected row", rows=[0])
+
+
+def test_mla_wide_groups_mixed_rows_and_a_rejected_row(env):
+    """Workgroups of 64 query vectors over several rows: H=16 and 9 rows per
+    sequence (144 vectors, so the last workgroup of a sequence has one active
+    wave pair of four), rows at different positions in one workgroup, and one
+    row at the capacity, which is not read: its outputs are zero and the sync
+    reports MK_ERR_INVALID_ARG; every other row matches the oracle."""
+    import moe_layer_stack_amd as mk
+    torch = env
+    cap = 1200
+    pos = [1199 - 37 * r for r in range(9)] + [3 + 50 * r for r in range(9)]
+    pos[13] = cap  # rejected
+    _say(f"MLA H=16, 2 sequences x 9 rows, capacity {cap}, row 13 rejected")
+    outs, q, cache, info = _run(torch, 16, pos, 9, 2, cap, calls=2)
+    for o, rc in outs:
+        assert rc == mk.MK_ERR_INVALID_ARG
+        assert (o[13] == 0).all()
+        _check(o, q, cache, pos, 9, SCALE, f"sequence 0 of 2 x 9 rows, {info.splits} splits", rows=range(9))
+        # sequence 1 without the rejected row (the oracle rows must stay valid)
+        keep = [r for r in range(9, 18) if r != 13]
+        _check(o, q, cache, pos, 9, SCALE, "sequence 1 beside the rejected row", rows=keep, seq0=1)
