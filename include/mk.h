@@ -58,7 +58,11 @@
  *
  * Concurrency.  A handle's workspace is shared by its launches: do not run
  * steps of one handle on two streams at once.  Several handles may share the
- * same weights (e.g. batch 1 and batch 8 over one stack).
+ * same weights (e.g. batch 1 and batch 8 over one stack).  A step is a launch
+ * of one workgroup per CU, each taking the CU's whole LDS, whose workgroups
+ * wait for each other at grid barriers: kernels running beside it on other
+ * streams delay its start on the CUs they hold, and a step whose workgroups
+ * do not all arrive within the watchdog ends with MK_ERR_TIMEOUT.
  */
 #ifndef MK_H
 #define MK_H

@@ -126,7 +126,7 @@ struct KParams {
 
 }  // namespace mk
 
-// One cooperative launch of the kernel that p selects.  Returns 0, a
+// One launch (one workgroup per CU) of the kernel that p selects.  Returns 0, a
 // hipError_t of the launch (> 0), -1 (device query or the dynamic-LDS
 // attribute failed), -2 (geometry outside the instantiations) or -3 (the
 // kernel declares static LDS).

@@ -1,5 +1,5 @@
 // mk_runtime.hip -- host side of libmk.so: argument validation, workspace,
-// the device copy of the weight-pointer table, the cooperative launch, and
+// the device copy of the weight-pointer table, the launch, and
 // device-error reporting.  See include/mk.h for the contract.
 #include <hip/hip_runtime.h>
 
@@ -203,7 +203,6 @@ int mk_create(const mk_config* cfg, const mk_layer_weights* layers, mk_handle** 
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MK_ERR_DEVICE, "hipGetDeviceProperties failed");
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(MK_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
-  if (!prop.cooperativeLaunch) return fail(MK_ERR_DEVICE, "device lacks cooperative launch");
   if (prop.maxSharedMemoryPerMultiProcessor < (size_t)mk::kLdsTotal)
     return fail(MK_ERR_DEVICE, "device has %zu bytes of LDS per CU, need %d", prop.maxSharedMemoryPerMultiProcessor,
                 mk::kLdsTotal);
