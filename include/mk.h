@@ -60,9 +60,14 @@
  * steps of one handle on two streams at once.  Several handles may share the
  * same weights (e.g. batch 1 and batch 8 over one stack).  A step is a launch
  * of one workgroup per CU, each taking the CU's whole LDS, whose workgroups
- * wait for each other at grid barriers: kernels running beside it on other
- * streams delay its start on the CUs they hold, and a step whose workgroups
- * do not all arrive within the watchdog ends with MK_ERR_TIMEOUT.
+ * wait for each other at grid barriers, so two steps must not run at the
+ * same time: the library orders the steps of all handles on a device (a step
+ * enqueued on another stream than the device's previous step waits for that
+ * step on the GPU).  Steps enqueued while their stream captures a graph are
+ * not ordered: replays of such graphs on different streams must not overlap.
+ * Kernels of other code running beside a step delay its start on the CUs
+ * they hold; a step whose workgroups do not all arrive within the watchdog
+ * ends with MK_ERR_TIMEOUT.
  */
 #ifndef MK_H
 #define MK_H

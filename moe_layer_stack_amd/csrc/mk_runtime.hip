@@ -398,6 +398,24 @@ int mk_get_info(const mk_handle* h, mk_info* info) {
 
 namespace {
 
+// A step needs every CU at once: one workgroup per CU, each holding the CU's
+// whole LDS, and grid barriers that wait for all of them.  Two steps running
+// at the same time on different streams would each hold part of the CUs and
+// wait at their first barrier for workgroups that cannot be placed, until
+// the watchdog ends both.  So the steps of all handles on one device are
+// ordered: an event is recorded after every step, and a step enqueued on
+// another stream than the device's previous step first waits for it.  Steps
+// on one stream need no wait.  A stream that is capturing a graph takes no
+// part (graph replays on different streams must not overlap).
+struct StepOrder {
+  std::mutex mu;
+  hipEvent_t ev = nullptr;  // created on first use, kept until the process ends
+  hipStream_t last = nullptr;
+  bool any = false;
+};
+constexpr int kOrderDevices = 64;
+StepOrder g_order[kOrderDevices];
+
 int launch_status(int e) {
   if (e == -2) return fail(MK_ERR_UNSUPPORTED, "launch geometry out of range");
   if (e == -3) return fail(MK_ERR_HIP, "the kernel declares static LDS, which leaves no room for its ring");
@@ -428,6 +446,18 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return fail(MK_ERR_INVALID_ARG, "current device differs from the handle's device");
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return fail(MK_ERR_HIP, "querying the stream's capture state failed");
+  StepOrder* so = (cap == hipStreamCaptureStatusNone && dev < kOrderDevices) ? &g_order[dev] : nullptr;
+  std::unique_lock<std::mutex> order_lock;
+  if (so) {
+    order_lock = std::unique_lock<std::mutex>(so->mu);
+    if (!so->ev && hipEventCreateWithFlags(&so->ev, hipEventDisableTiming) != hipSuccess)
+      return fail(MK_ERR_HIP, "creating the step-order event failed");
+    if (so->any && so->last != hs && hipStreamWaitEvent(hs, so->ev, 0) != hipSuccess)
+      return fail(MK_ERR_HIP, "ordering the step after the previous step on another stream failed");
+  }
   const int Mg = launch_rows(c);
   // the persistent kernel runs all row groups in one launch when the handle
   // allows it; the phase launches take one row group at a time
@@ -488,6 +518,11 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
         if (st != MK_OK) return st;
       }
     }
+  }
+  if (so) {
+    if (hipEventRecord(so->ev, hs) != hipSuccess) return fail(MK_ERR_HIP, "recording the step-order event failed");
+    so->last = hs;
+    so->any = true;
   }
   return MK_OK;
 }
