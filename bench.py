@@ -470,11 +470,13 @@ def only_leg(torch, mk, args):
         w = MOE16_B8.with_(name=leg, M=M)
         r = run_leg(torch, mk, st, w, M, 1, args.steps, args.warmup, trace_union=M > 1)
     else:
-        M, rps = {"batch1": (1, 1), "batch8": (8, 1), "verify8": (8, 8), "verify64": (64, 8)}[leg]
+        M, rps = {"batch1": (1, 1), "batch8": (8, 1), "verify8": (8, 8), "verify64": (64, 8),
+                  "phased_b1": (1, 1)}[leg]
         w8 = ATTN92_B8.with_(cap_extra=max(64, 8 * (args.warmup + args.steps + 2)))
         st = DeviceStack(w8, n_layers=args.layers)
         w = w8.with_(M=M, rows_per_seq=rps)
-        r = run_leg(torch, mk, st, w, M, rps, args.steps, args.warmup, trace_union=M > 1)
+        r = run_leg(torch, mk, st, w, M, rps, args.steps, args.warmup, trace_union=M > 1,
+                    phased=leg.startswith("phased"))
     log(f"{leg}: {r['ms_per_step']:.3f} ms/step, {r['achieved_gbps']:.0f} GB/s algorithmic "
         f"({100 * r['frac']:.1f}% of peak), {r['launches']} launch(es) per step")
     if args.calib_copy_mib:
@@ -509,7 +511,8 @@ def main():
     ap.add_argument("--maps-out", default=None,
                     help="after the teardown, copy /proc/self/maps to this file (to name the owner of an address "
                          "in a crash report at exit)")
-    ap.add_argument("--only", choices=["batch1", "batch8", "verify8", "verify64", "moe16_b1", "moe16_b8", "mla"],
+    ap.add_argument("--only", choices=["batch1", "batch8", "verify8", "verify64", "moe16_b1", "moe16_b8", "mla",
+                                       "phased_b1"],
                     default=None, help="run only this leg (and --calib-copy-mib), print its record as JSON: the "
                                        "program of a counter pass")
     ap.add_argument("--pmc-kernel", default="1, 1>",
