@@ -526,7 +526,7 @@ def main():
                   args.pmc_out)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the decode kernel runs on a single MI355X and this build has no "
+        print(f"bench.py measures one GPU: the decode kernel runs on a single MI355X and the library has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch
