@@ -57,6 +57,29 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
 }
 __device__ __forceinline__ short bf16_bits(__bf16 h) { return __builtin_bit_cast(short, h); }
 
+// Workgroup b's (sequence, query group, split).  The QG workgroups of one
+// (sequence, split) pair read the same cache tiles, and workgroups are dealt
+// to the 8 XCDs round-robin by index, so in each block of 8 pairs the QG
+// workgroups of a pair take indices 8 apart: one XCD, whose L2 then serves
+// each tile to all of them.  The last (pairs % 8) pairs take consecutive
+// indices.  Any such numbering computes the same results.
+__device__ __forceinline__ void wg_coords(const Params& p, int b, int& seq, int& qg, int& s) {
+  const int QG = p.QG, U = (int)gridDim.x / QG;  // (sequence, split) pairs
+  const int head = (U & ~7) * QG;                  // workgroups of the full blocks
+  int u;
+  if (b < head) {
+    const int blk = b / (8 * QG), r = b % (8 * QG);
+    qg = r >> 3;
+    u = blk * 8 + (r & 7);
+  } else {
+    const int t = b - head, rest = U & 7;
+    qg = t / rest;
+    u = (U & ~7) + t % rest;
+  }
+  seq = u / p.S;
+  s = u % p.S;
+}
+
 // Few query vectors per sequence (decode: H of one row): workgroups of 16
 // vectors, two per CU, the 576 key columns split over the 4 waves.
 namespace q16 {
@@ -118,7 +141,8 @@ __global__ void __launch_bounds__(kThreads, 2) split_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char tile[kTile * kPitch];
   __shared__ __attribute__((aligned(16))) f32x4_t exch[2][kWaves][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int s = blockIdx.x % p.S, qg = (blockIdx.x / p.S) % p.QG, seq = blockIdx.x / (p.S * p.QG);
+  int seq, qg, s;
+  wg_coords(p, (int)blockIdx.x, seq, qg, s);
   const int row = seq * p.rps + (qg * kQ) / p.H;
   const int pos = p.positions[row];
   const bool ok = pos >= 0 && pos < p.cap;
@@ -354,7 +378,8 @@ __global__ void __launch_bounds__(kThreads, 1) split_kernel(Params p) {
   f32x4_t* exch = reinterpret_cast<f32x4_t*>(lds + 2 * kTileLds);  // [wave][2][64]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int pr = wave >> 1, hf = wave & 1;
-  const int s = blockIdx.x % p.S, qg = (blockIdx.x / p.S) % p.QG, seq = blockIdx.x / (p.S * p.QG);
+  int seq, qg, s;
+  wg_coords(p, (int)blockIdx.x, seq, qg, s);
   const int nqs = p.H * p.rps;  // query vectors of a sequence
   // positions attended by each pair's row; the workgroup's tiles cover the longest
   int npos_w = 0, npos_max = 0;
