@@ -463,7 +463,8 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
   // allows it; the phase launches take one row group at a time
   const bool grouped = !phased && h->n_groups > 1;
   const int n_launch = grouped ? 1 : c.rows / Mg;
-  for (int gi = 0; gi < n_launch; ++gi) {
+  int rc = MK_OK;
+  for (int gi = 0; gi < n_launch && rc == MK_OK; ++gi) {
     KParams p{};
     p.L = c.n_layers; p.d = c.d_model; p.E = c.n_experts; p.k = c.top_k; p.S = c.n_shared; p.F = c.d_ff;
     p.attn = c.has_attn ? 1 : 0;
@@ -503,28 +504,28 @@ int run_step(mk_handle* h, const float* hidden_in, const int32_t* positions, con
       p.stamps = reinterpret_cast<long long*>(h->stamps);
       p.only_l = 0;
       p.only_ph = -1;
-      const int st = launch_status(mk_launch_kernel(&p, stream));
-      if (st != MK_OK) return st;
+      rc = launch_status(mk_launch_kernel(&p, stream));
       continue;
     }
     p.stamps = nullptr;
     const int ph0 = c.has_attn ? mk::PH_QKV : mk::PH_RS;
     const int ph1 = Mg > 1 ? mk::PH_DOWNB : mk::PH_DOWN;
-    for (int l = 0; l < c.n_layers; ++l) {
-      for (int ph = ph0; ph <= ph1; ++ph) {
+    for (int l = 0; l < c.n_layers && rc == MK_OK; ++l) {
+      for (int ph = ph0; ph <= ph1 && rc == MK_OK; ++ph) {
         p.only_l = l;
         p.only_ph = ph;
-        const int st = launch_status(mk_launch_kernel(&p, stream));
-        if (st != MK_OK) return st;
+        rc = launch_status(mk_launch_kernel(&p, stream));
       }
     }
   }
+  // recorded after a failed launch too: launches before it may be running
   if (so) {
-    if (hipEventRecord(so->ev, hs) != hipSuccess) return fail(MK_ERR_HIP, "recording the step-order event failed");
+    if (hipEventRecord(so->ev, hs) != hipSuccess)
+      return rc != MK_OK ? rc : fail(MK_ERR_HIP, "recording the step-order event failed");
     so->last = hs;
     so->any = true;
   }
-  return MK_OK;
+  return rc;
 }
 
 }  // namespace
