@@ -44,3 +44,14 @@ def test_union_and_fp32_accounting():
     assert got == sum((u + 1) * b_e + 2048 * 64 * 2 for u in unions)
     # the fp32 stack: 4-byte weights, no shared expert, no attention
     assert bench.step_bytes(TINY, 1, 1, [2, 2], 0) == 2 * (2 * 3 * 256 * 512 * 4 + 256 * 8 * 4)
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: asked for more, it exits with status 2 and a
+    message, before touching a device."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2, (r.returncode, r.stderr[-500:])
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+    assert r.stdout == ""
