@@ -350,10 +350,34 @@ def cpu_model():
     return name, n
 
 
-def cpu_baseline(torch, st, w, n_layers_sample, threads=None):
+def gpu_step_b1(torch, mk, st, w):
+    """One batch-1 step of the decode kernel on the input the CPU leg uses
+    (row 0 of hidden(0), position w.past, sequence 0 of the cache), with its
+    routing traced: (output [1][d] fp64, expert ids [L][1][k])."""
+    import numpy as np
+    h = mk.mk_create(st.config(rows=1, rows_per_seq=1), st.layer_weights())
+    try:
+        ids = torch.zeros(st.L, 1, w.k, dtype=torch.int32, device="cuda")
+        mk.mk_set_trace(h, ids.data_ptr(), 0, 0)
+        x = st.hidden(0)[:1].contiguous()
+        out = torch.empty_like(x)
+        pos = torch.tensor([w.past], dtype=torch.int32, device="cuda")
+        mk.mk_decode_step(h, x.data_ptr(), pos.data_ptr(), st.kv(), out.data_ptr(), 0)
+        rc = mk.mk_sync(h, 0)
+        if rc != mk.MK_OK:
+            raise mk.MkError(rc, mk.mk_last_error())
+        return out.cpu().numpy().astype(np.float64), ids.cpu().numpy()
+    finally:
+        mk.mk_destroy(h)
+
+
+def cpu_baseline(torch, st, w, n_layers_sample, threads=None, gpu=None):
     """The CPU oracle (as it stands) on the first layers of a batch-1 step:
     host copies of the touched tensors are made before the timer starts.
-    threads: the oracle's thread count for this sample (default: all)."""
+    threads: the oracle's thread count for this sample (default: all).
+    gpu: (output, expert ids) of the same step on the GPU (gpu_step_b1); with
+    the whole step sampled, the result then carries a parity verdict of the
+    GPU output against the oracle's (which routes by itself)."""
     import numpy as np
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -364,6 +388,7 @@ def cpu_baseline(torch, st, w, n_layers_sample, threads=None):
     h = st.hidden(0)[:1].cpu().numpy().astype(np.float64)
     pos = [w.past]
     t_compute = 0.0
+    ids_differ = []
     for l in range(n_layers_sample):
         H = st.host_layer(l, experts=[])  # attention, router, shared
         kv = oracle.OracleKV(st.to_host(st.kc[l, :1]), st.to_host(st.vc[l, :1]))
@@ -372,6 +397,8 @@ def cpu_baseline(torch, st, w, n_layers_sample, threads=None):
         h1 = oracle.attn_block(dims, ly, h, pos, kv)
         _, ids, wts, _ = oracle.route(dims, ly, h1)
         t_compute += time.perf_counter() - t0
+        if gpu is not None and set(np.asarray(ids[0]).tolist()) != set(gpu[1][l, 0].tolist()):
+            ids_differ.append(l)
         H = st.host_layer(l, experts=ids[0])
         ly = oracle_layer(H)
         t0 = time.perf_counter()
@@ -382,10 +409,20 @@ def cpu_baseline(torch, st, w, n_layers_sample, threads=None):
     per_layer = t_compute / n_layers_sample
     step_s = per_layer * w.L
     model, n_avail = cpu_model()
-    return dict(value=1.0 / step_s, unit="tokens/s", cores=used, kind="oracle", cpu_model=model,
-                cpus_available=n_avail,
-                sample=f"first {n_layers_sample} of {w.L} layers of one batch-1 step (fp64 C oracle, OpenMP over "
-                       f"output rows); compute time {t_compute:.1f} s, scaled by {w.L}/{n_layers_sample}")
+    res = dict(value=1.0 / step_s, unit="tokens/s", cores=used, kind="oracle", cpu_model=model,
+               cpus_available=n_avail,
+               sample=f"first {n_layers_sample} of {w.L} layers of one batch-1 step (fp64 C oracle, OpenMP over "
+                      f"output rows); compute time {t_compute:.1f} s, scaled by {w.L}/{n_layers_sample}")
+    if gpu is not None and n_layers_sample == w.L:
+        from parity_util import compare, tolerances
+        c = compare(gpu[0], h)
+        tol = tolerances(w)
+        res["parity"] = dict(rows=1, layers=w.L, max_abs=c["max_abs"], rel_l2=c["rel_l2"],
+                             tol_max_abs=tol["max_abs"], tol_rel_l2=tol["rel_l2"],
+                             expert_sets_differ=len(ids_differ), first_differing_layer=(ids_differ or [None])[0],
+                             ok=bool(c["max_abs"] <= tol["max_abs"] and c["rel_l2"] <= tol["rel_l2"]
+                                     and not ids_differ))
+    return res
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn92_b1.json")
@@ -637,9 +674,15 @@ def main():
     if not args.no_cpu_baseline:
         def cpu_leg():
             nonlocal cpu
+            gpu = gpu_step_b1(torch, mk, st, w1)
             t0 = time.perf_counter()
-            cpu = cpu_baseline(torch, st, w1, min(args.cpu_layers, st.L))
+            cpu = cpu_baseline(torch, st, w1, min(args.cpu_layers, st.L), gpu=gpu)
             log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads ({time.perf_counter() - t0:.1f} s)")
+            if "parity" in cpu:
+                pv = cpu["parity"]
+                log(f"parity of the batch-1 step against the oracle ({pv['layers']} layers): max_abs "
+                    f"{pv['max_abs']:.2e}, rel_l2 {pv['rel_l2']:.2e}, expert sets differing in "
+                    f"{pv['expert_sets_differ']} layers, {'ok' if pv['ok'] else 'NOT ok'}")
             if args.cpu_layers_1t > 0:
                 t0 = time.perf_counter()
                 one = cpu_baseline(torch, st, w1, min(args.cpu_layers_1t, st.L), threads=1)
@@ -677,6 +720,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(b1["achieved_gbps"], 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(b1["frac"], 4), "traffic": traffic,
                      "bytes_per_launch": b1["bytes_per_step"]},
+        "parity": cpu.pop("parity", None) if cpu else None,
         "cpu_baseline": cpu,
         "batch1": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b1.items()},
         "batch8": None if b8 is None else {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b8.items()},
